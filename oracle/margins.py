@@ -1,0 +1,93 @@
+"""Oracle: decision margins for tie-following parity.
+
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+Every discrete decision of the append path gets a relative margin, computed in
+float64.  A decision whose margin is below TIE (1e-6) is a documented tie: a
+faithful implementation in other arithmetic may take either side, and the
+checker then adopts the implementation's choice and recomputes everything
+downstream before demanding bit-exactness again.
+
+Kinds
+  cand   : |D_(Kc) - D_(Kc+1)| / max    (QSAC candidate-set boundary)
+  choice : |P_(1) - P_(2)| / max         (QSAC final choice; D for argmin modes)
+  c32    : distance of c to the nearest binary32 rounding midpoint / |c|
+  sigma  : distance of fl32(a/127) to the nearest binary16 midpoint / sigma
+  int8   : |c32/sigma - (n + 1/2)| sigma / a for the nearest half-integer
+"""
+import numpy as np
+
+TIE = 1e-6
+
+
+def _rel(a, b):
+    den = np.maximum(np.abs(a), np.abs(b))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.abs(a - b) / den
+    return np.where(den == 0, 0.0, out)
+
+
+def argmin_margin(dist):
+    """Relative gap between the two smallest entries of each row."""
+    if dist.shape[1] < 2:
+        return np.full(dist.shape[0], np.inf)
+    part = np.partition(dist, 1, axis=1)
+    return _rel(part[:, 0], part[:, 1])
+
+
+def key_margins(info, top_k, flags, no_range_flag=2):
+    """Per-token min margin over the QSAC decisions (cand, choice)."""
+    dist = info["D"]
+    n, c_count = dist.shape
+    if info.get("cand") is None:
+        m = argmin_margin(dist)
+        return dict(cand=np.full(n, np.inf), choice=m)
+    kc = info["cand"].shape[1]
+    srt = np.sort(dist, axis=1)
+    cand = _rel(srt[:, kc - 1], srt[:, kc]) if kc < c_count else np.full(n, np.inf)
+    p = info["P"]
+    if kc < 2:
+        choice = np.full(n, np.inf)
+    else:
+        ps = np.sort(p, axis=1)
+        choice = _rel(ps[:, 0], ps[:, 1])
+    return dict(cand=cand, choice=choice)
+
+
+def _midpoint_margin_f32(c):
+    c = np.asarray(c, np.float64)
+    c32 = c.astype(np.float32)
+    nxt = np.nextafter(c32, np.float32(np.inf) * np.sign(c32 + (c32 == 0)))
+    ulp = np.abs(nxt.astype(np.float64) - c32.astype(np.float64))
+    dist = np.abs(np.abs(c - c32.astype(np.float64)) - ulp / 2)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return np.where(c == 0, np.inf, dist / np.abs(c))
+
+
+def _midpoint_margin_f16(y32):
+    y = np.asarray(y32, np.float64)
+    h = y.astype(np.float16)
+    nxt = np.nextafter(h, np.float16(np.inf))
+    ulp = np.abs(nxt.astype(np.float64) - h.astype(np.float64))
+    dist = np.abs(np.abs(y - h.astype(np.float64)) - ulp / 2)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return np.where(h == 0, np.inf, dist / np.abs(h.astype(np.float64)))
+
+
+def psac_margins(c_exact, coef_scale):
+    """Per-token minimum margins of the PSAC roundings (c32, sigma, int8)."""
+    n = c_exact.shape[0]
+    if c_exact.shape[1] == 0:
+        inf = np.full(n, np.inf)
+        return dict(c32=inf, sigma=inf, int8=inf)
+    c32m = _midpoint_margin_f32(c_exact).min(axis=1)
+    c32 = c_exact.astype(np.float32)
+    a = np.abs(c32).max(axis=1).astype(np.float64)
+    y = (a / 127.0).astype(np.float32)
+    sig = _midpoint_margin_f16(y)
+    sg = np.asarray(coef_scale, np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        x = (c32.astype(np.float64) / sg[:, None]).astype(np.float32).astype(np.float64)
+        frac = np.abs(x - (np.floor(x) + 0.5))
+        i8 = np.where(sg[:, None] > 0, frac * sg[:, None] / a[:, None], np.inf).min(axis=1)
+    return dict(c32=c32m, sigma=sig, int8=i8)

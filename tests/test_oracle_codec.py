@@ -1,0 +1,221 @@
+"""Pins of the oracle's quantize-append (CPU only)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import calibrate as oc
+from oracle import codec
+from oracle import attention as oa
+from oracle.numerics import bf16, fl32, fp16_of_f32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = workloads.WORKLOADS["tiny"]
+    d = workloads.generate(w)
+    cal = oc.calibrate(d["q_hist"], d["k_hist"], d["v_hist"], 16, 16, 8, "f32", seed=11)
+    return w, d, cal
+
+
+def test_bf16_rounding_against_bit_rounding():
+    """bfloat16 RNE from float64 equals rounding the float32 pattern when the
+    float32 step is exact, and handles ties to even."""
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.14159, 1e-3, 65504.0])
+    got = bf16(x)
+    assert got[1] == 1.0                     # tie -> even (1.0)
+    assert got[2] == 1.0 + 2**-6            # tie -> even (1 + 2^-6)
+    b = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    rnd = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    assert np.array_equal(got.view(np.uint32), rnd.astype(np.uint32))
+
+
+def test_int2_golden_example():
+    g = json.load(open(os.path.join(GOLDEN, "int2_worked.json")))
+    rho = np.array(g["rho"], np.float32)[None, :]
+    z, s = codec.int2_params(rho)
+    assert (z, s) == (g["z"], g["s"])
+    codes = codec.int2_encode(rho, z, s)
+    assert codes[0].tolist() == g["codes"]
+    assert codec.int2_decode(codes, z, s)[0].tolist() == g["rho_hat"]
+    assert int(codec.pack_codes(codes)[0, 0]) == int(g["packed_hex"], 16)
+    assert np.array_equal(codec.unpack_codes(codec.pack_codes(codes), 16), codes)
+
+
+def test_int8_golden_example():
+    g = json.load(open(os.path.join(GOLDEN, "int8_worked.json")))
+    c = np.array(g["c"])
+    r = len(c)
+    u = np.eye(r)                      # e = c along an orthonormal basis
+    n, sigma, _ = codec.psac(c[None, :], np.zeros((1, r)), np.zeros((1, r)), u)
+    assert float(sigma[0]) == g["sigma"]
+    assert n[0].tolist() == g["n"]
+
+
+def test_invariant_a_qvg_mode_is_nearest(tiny):
+    w, d, cal = tiny
+    k = d["k"][0]
+    mu = cal["mu_k"][0]
+    idx, _ = codec.select_keys(k, mu, cal["sens"][0], 4, codec.QVG_MODE)
+    for t in range(k.shape[0]):
+        best, bd = -1, np.inf
+        for c in range(mu.shape[0]):
+            dd = sum((float(k[t, j]) - float(mu[c, j])) ** 2 for j in range(k.shape[1]))
+            if dd < bd:
+                best, bd = c, dd
+        assert idx[t] == best
+
+
+def test_no_range_term_is_weighted_nearest(tiny):
+    w, d, cal = tiny
+    k, mu, s = d["k"][0], cal["mu_k"][0], cal["sens"][0].astype(np.float64)
+    idx, _ = codec.select_keys(k, mu, s, 4, codec.NO_RANGE_TERM)
+    for t in range(0, k.shape[0], 7):
+        dd = [sum(s[j] * (float(k[t, j]) - float(mu[c, j])) ** 2 for j in range(64)) for c in range(16)]
+        assert idx[t] == int(np.argmin(dd))
+
+
+def test_invariant_d_all_candidates_is_global_argmin(tiny):
+    """K_c = C: QSAC's choice is the brute-force argmin of P over all centres
+    (ties: smaller D, lower index)."""
+    w, d, cal = tiny
+    k, mu, s = d["k"][0], cal["mu_k"][0], cal["sens"][0].astype(np.float64)
+    sg = [sum(s[16 * g:16 * g + 16]) for g in range(4)]
+    idx, _ = codec.select_keys(k, mu, s, 16, 0)
+    for t in range(0, k.shape[0], 5):
+        best = None
+        for c in range(16):
+            rho = [float(np.float32(float(k[t, j]) - float(mu[c, j]))) for j in range(64)]
+            p = sum(sg[g] * (max(rho[16 * g:16 * g + 16]) - min(rho[16 * g:16 * g + 16])) ** 2
+                    for g in range(4)) / 108.0
+            dd = sum(s[j] * (float(k[t, j]) - float(mu[c, j])) ** 2 for j in range(64))
+            key = (p, dd, c)
+            if best is None or key < best:
+                best = key
+        assert idx[t] == best[2]
+
+
+def test_qsac_lowers_weighted_int2_error():
+    """Statistical sanity (not parity): the sensitivity-weighted INT2 error
+    of QSAC is no larger on average than nearest-centre assignment."""
+    w = workloads.scaled(workloads.WORKLOADS["matrix_game"], heads=1, frames=2)
+    d = workloads.generate(w)
+    cal = oc.calibrate(d["q_hist"], d["k_hist"], d["v_hist"], 64, 64, 8, "bf16", seed=3, iters=4)
+    k = d["k"][0]
+    s = cal["sens"][0].astype(np.float64)
+    errs = {}
+    for name, flags in (("qsac", 0), ("qvg", codec.QVG_MODE)):
+        out = codec.append_keys(k, cal["mu_k"][0], cal["sens"][0], cal["u"][0][:, :0],
+                                w.frame_tokens, 16, 4, flags)
+        e = out["rho"].astype(np.float64) - out["rho_hat"].astype(np.float64)
+        errs[name] = np.mean((e * e) @ s)
+    assert errs["qsac"] <= errs["qvg"]
+
+
+def _ulp32(x):
+    x = np.abs(np.asarray(x, np.float32))
+    return (np.nextafter(x, np.float32(np.inf)) - x).astype(np.float64)
+
+
+@pytest.mark.parametrize("fp32_params", [False, True])
+def test_invariant_b_int2_error_bound(tiny, fp32_params):
+    w, d, cal = tiny
+    flags = codec.FP32_PARAMS_TEST if fp32_params else 0
+    out = codec.append_keys(d["k"][0], cal["mu_k"][0], cal["sens"][0], cal["u"][0],
+                            64, 16, 4, flags)
+    rho, rho_hat = out["rho"], out["rho_hat"]
+    for p, (a, b) in enumerate(codec.frame_tiles(128, 64, 16)):
+        for g in range(4):
+            blk = rho[a:b, 16 * g:16 * g + 16].astype(np.float64)
+            hat = rho_hat[a:b, 16 * g:16 * g + 16].astype(np.float64)
+            m, mx = blk.min(), blk.max()
+            rng = mx - m
+            err = np.abs(blk - hat)
+            slack = 2 * _ulp32(blk)
+            if fp32_params:
+                bound = rng / 6 * (1 + 2**-20) + slack
+            else:
+                z, s = out["z"][p, g], out["s"][p, g]
+                bound = rng / 6 + abs(z - m) + 1.5 * abs(s - rng / 3) + slack
+            assert np.all(err <= bound)
+            codes = out["codes"][a:b, 16 * g:16 * g + 16]
+            assert codes.max() <= 3
+            # idempotence: re-quantizing the decoded values gives the codes back
+            z, s = out["z"][p, g], out["s"][p, g]
+            assert np.array_equal(codec.int2_encode(hat.astype(np.float32), z, s), codes)
+            if fp32_params and rng > 0:
+                assert codes[blk == m].max() == 0 and codes[blk == mx].min() == 3
+
+
+def test_invariant_c_rank0_is_qvg_reconstruction(tiny):
+    w, d, cal = tiny
+    k = d["k"][0]
+    u0 = np.zeros((64, 0), np.float32)
+    out = codec.append_keys(k, cal["mu_k"][0], cal["sens"][0], u0, 64, 16, 4, 0)
+    rec = oa.reconstruct_keys(out["idx"], out["codes"], out["z"], out["s"], out["coef"],
+                              out["coef_scale"], cal["mu_k"][0], u0, 64, 16)
+    expect = cal["mu_k"][0][out["idx"]].astype(np.float64) + out["rho_hat"].astype(np.float64)
+    assert np.array_equal(rec, expect)
+
+
+def test_invariant_c_full_rank_removes_error(tiny):
+    """U a full orthonormal basis: ||k - k~|| = ||c - c_hat|| <= sqrt(d) sigma/2."""
+    w, d, cal = tiny
+    k = d["k"][0]
+    rng = np.random.default_rng(5)
+    u = fl32(np.linalg.qr(rng.standard_normal((64, 64)))[0])
+    out = codec.append_keys(k, cal["mu_k"][0], cal["sens"][0], u, 64, 16, 4, 0)
+    rec = oa.reconstruct_keys(out["idx"], out["codes"], out["z"], out["s"], out["coef"],
+                              out["coef_scale"], cal["mu_k"][0], u, 64, 16)
+    err = np.linalg.norm(k.astype(np.float64) - rec, axis=1)
+    sig = out["coef_scale"].astype(np.float64)
+    # U is orthonormal only to float32 rounding: allow that slack
+    e_norm = np.linalg.norm(k.astype(np.float64) - cal["mu_k"][0][out["idx"]] - out["rho_hat"], axis=1)
+    assert np.all(err <= np.sqrt(64) * sig / 2 + 1e-5 * e_norm + 1e-12)
+    qvg_err = e_norm
+    assert np.mean(err) < 0.2 * np.mean(qvg_err)
+
+
+def test_psac_projection_bound_any_rank(tiny):
+    """|U^T (k - k~)|_inf <= sigma/2 (+ float32 U slack), since U^T U = I."""
+    w, d, cal = tiny
+    k = d["k"][0]
+    u = cal["u"][0]
+    out = codec.append_keys(k, cal["mu_k"][0], cal["sens"][0], u, 64, 16, 4, 0)
+    rec = oa.reconstruct_keys(out["idx"], out["codes"], out["z"], out["s"], out["coef"],
+                              out["coef_scale"], cal["mu_k"][0], u, 64, 16)
+    proj = np.abs((k.astype(np.float64) - rec) @ u.astype(np.float64)).max(axis=1)
+    e_norm = np.linalg.norm(k.astype(np.float64) - cal["mu_k"][0][out["idx"]] - out["rho_hat"], axis=1)
+    assert np.all(proj <= out["coef_scale"] / 2 + 1e-5 * e_norm)
+    # and for q in span(U): |q.k~ - q.k| <= ||U^T q||_1 sigma / 2 (+ slack)
+    qc = rng_q = np.random.default_rng(2).standard_normal(8)
+    q = u.astype(np.float64) @ qc
+    diff = np.abs((rec - k.astype(np.float64)) @ q)
+    assert np.all(diff <= np.abs(u.astype(np.float64).T @ q).sum() * out["coef_scale"] / 2
+                  + 1e-5 * e_norm * np.abs(q).sum())
+
+
+def test_values_nearest_and_int2(tiny):
+    w, d, cal = tiny
+    v, mu = d["v"][0], cal["mu_v"][0]
+    out = codec.append_values(v, mu, 64, 16)
+    for t in range(0, v.shape[0], 3):
+        dd = [sum((float(v[t, j]) - float(mu[c, j])) ** 2 for j in range(64)) for c in range(16)]
+        assert out["idx"][t] == int(np.argmin(dd))
+    assert np.array_equal(out["rho"], fl32(v.astype(np.float64) - mu[out["idx"]]))
+
+
+def test_frame_tiles_ragged():
+    t = codec.frame_tiles(2 * 1560, 1560, 16)
+    assert len(t) == 2 * 98
+    assert t[97] == (1552, 1560) and t[98] == (1560, 1576)
+
+
+def test_fp16_of_f32_rne():
+    # 1 + 2^-11 is the midpoint between 1 and 1 + 2^-10 in binary16 -> even (1)
+    assert fp16_of_f32(np.float32(1 + 2**-11)) == 1.0
+    assert fp16_of_f32(np.float32(1 + 3 * 2**-11)) == 1 + 2**-9
