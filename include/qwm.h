@@ -1,0 +1,284 @@
+/*
+ * qwm.h -- C ABI of a QuantWM 2-bit KV-cache library for AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * The method is QuantWM ("QuantWM: Temporally Consistent 2-Bit KV Cache
+ * Quantization for Video World Models", arXiv 2609.26425), known here through
+ * the pages that report it:
+ *   [digest]   "Flickering after quantization? A temporally stable 2-bit KV
+ *              Cache compression framework for video world models emerges"
+ *              (English news digest; paragraphs on QSAC, PSAC, the systems
+ *              implementation and the attention analysis),
+ *   [abstract] the Hugging Face Daily Papers abstract of the paper,
+ *   [review]   "QuantWM: Temporally Consistent 2-Bit KV Cache Quantization for
+ *              World Models and Video Generation" (summary; Eq. 7; FAQ).
+ * A per-layer KV cache of already-generated frames grows with every frame
+ * ([digest], opening paragraph).  Each cached Key is stored as a cluster
+ * centre plus a 2-bit residual; the centre is chosen by QSAC, and the Key
+ * error left after INT2 is compensated by PSAC along the principal directions
+ * of historical Queries ([digest], QSAC and PSAC paragraphs).  Values take the
+ * plain centre + 2-bit residual path.  Attention reconstructs the cache on the
+ * fly ([digest], PSAC paragraph: compensation during cache reconstruction).
+ *
+ * Conventions
+ *  - Every pointer is DEVICE memory unless its comment says "host".
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls that only enqueue work return as soon as it is enqueued; the ones
+ *    marked "synchronous" wait for their stream before returning.
+ *  - The caller owns every buffer (calibration block, cache block, workspace,
+ *    inputs, outputs); the library never allocates device memory and keeps no
+ *    pointer past a call except inside the caller-owned qwm_cache handle.
+ *  - Activations are [heads][tokens][head_dim] tensors described by
+ *    qwm_strides in ELEMENTS: element (h, t, j) sits at base +
+ *    h*head + t*token + j.  The head_dim axis must be contiguous; the base
+ *    pointer and token*element_size must be multiples of 16 bytes.
+ *  - Errors are returned as negative status codes.  Every argument check runs
+ *    on the host before anything is enqueued: on error nothing is launched and
+ *    no cache counter moves.  Contents of device buffers are not inspected:
+ *    inputs outside the binary16 range (|x| >= 65504) or non-finite inputs give
+ *    unspecified values but never out-of-bounds accesses.
+ *  - No call is re-entrant for one cache; one stream per cache.
+ */
+#ifndef QWM_H
+#define QWM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QWM_ABI_VERSION 1
+
+/* status codes */
+#define QWM_OK 0
+#define QWM_ERR_INVALID_ARG (-1)  /* null pointer, bad size, stride or alignment */
+#define QWM_ERR_UNSUPPORTED (-2)  /* valid request outside what the kernels implement */
+#define QWM_ERR_ALIGN (-3)        /* append of a token count that is not whole frames */
+#define QWM_ERR_CAPACITY (-4)     /* append beyond max_frames, or workspace too small */
+#define QWM_ERR_STATE (-5)        /* K/V counters disagree, or handle from another config */
+#define QWM_ERR_HIP (-6)          /* a HIP runtime call failed; see qwm_status_string */
+
+/* io_dtype */
+#define QWM_BF16 0
+#define QWM_F32 1
+
+/* flags (ablation modes of the centre choice) */
+#define QWM_UNIFORM_SENS 1u   /* QSAC distances and scores with s = 1 */
+#define QWM_NO_RANGE_TERM 2u  /* choose argmin of the stage-1 distance (no INT2 score) */
+#define QWM_QVG_MODE 3u       /* both: nearest Euclidean centre, the QVG baseline */
+
+typedef struct qwm_config {
+  int32_t abi_version;      /* QWM_ABI_VERSION */
+  int32_t num_heads;        /* H >= 1 */
+  int32_t head_dim;         /* d: 64 or 128 */
+  int32_t frame_tokens;     /* F: tokens of one latent frame; appends are whole frames */
+  int32_t max_frames;       /* cache capacity in frames */
+  int32_t num_centroids_k;  /* C_K in [1, 512]: Key centres per head */
+  int32_t num_centroids_v;  /* C_V in [1, 512]: Value centres per head */
+  int32_t group_channels;   /* residual group width; must be 16 */
+  int32_t group_tokens;     /* T in {1,2,4,8,16,32}: tokens sharing one (zero, scale) */
+  int32_t top_candidates;   /* K_c in [0, 8]: QSAC stage-1 candidates (0: nearest) */
+  int32_t rank;             /* r in [0, 16]: PSAC principal directions */
+  int32_t io_dtype;         /* QWM_BF16 or QWM_F32 for activations and centres */
+  uint32_t flags;           /* QWM_UNIFORM_SENS | QWM_NO_RANGE_TERM */
+  int32_t reserved;         /* must be 0 */
+} qwm_config;
+
+typedef struct qwm_strides {
+  int64_t head;   /* elements between heads */
+  int64_t token;  /* elements between tokens (>= head_dim) */
+} qwm_strides;
+
+/*
+ * Byte sizes and offsets of the two caller-allocated blocks.
+ *
+ * Calibration block (per head h; all arrays [H][...] row-major):
+ *   mu_k   [H][C_K][d]  centres of Keys, io dtype (bf16 / fp32)
+ *   mu_v   [H][C_V][d]  centres of Values, io dtype
+ *   sens   [H][d]       fp32 s = diag(M), the Query second moment's diagonal
+ *   u      [H][d][r]    fp32 top-r eigenvectors of M (columns)
+ *   derived, filled by qwm_calib_import / qwm_calibrate:
+ *   u64    [H][d][r]    fp64 copy of u (exact)
+ *   sgroup [H][d/16]    fp64 S_g = sum of sens over group g
+ *   norm_kw [H][C_K]    fp32 ||mu||_s^2 / 2 (sensitivity-weighted)
+ *   norm_k  [H][C_K]    fp32 ||mu||^2 / 2
+ *   norm_v  [H][C_V]    fp32 ||mu||^2 / 2
+ *   head_max [H][4]     fp32 max_c ||mu_K||_s, max_c ||mu_K||, max_c ||mu_V||, 0
+ *
+ * Cache block (capacity N = max_frames*F tokens, P = max_frames*ceil(F/T)
+ * parameter tiles per head):
+ *   idx_k    [H][N]        u8 if C_K <= 256 else u16: chosen Key centre
+ *   codes_k  [H][N][d/16]  u32: 2-bit residual codes; word (t, g) holds the code
+ *                          of channel 16g+i in bits [2i, 2i+1]
+ *   params_k [H][P][d/16]  half2 (zero in the low half, scale in the high half)
+ *                          of tile p = frame*ceil(F/T) + (t mod F)/T
+ *   coef     [H][N][r]     int8 PSAC coefficients (absent when r = 0)
+ *   coef_scale [H][N]      fp16 per-token coefficient scale (absent when r = 0)
+ *   idx_v, codes_v, params_v  as above for Values.
+ * Every array starts on a 256-byte boundary.
+ */
+typedef struct qwm_layout_info {
+  uint64_t calib_bytes;
+  uint64_t cache_bytes;
+  uint64_t token_capacity;
+  uint64_t tile_capacity;
+  uint64_t mu_k, mu_v, sens, u, u64, sgroup, norm_kw, norm_k, norm_v, head_max;
+  uint64_t idx_k, codes_k, params_k, coef, coef_scale, idx_v, codes_v, params_v;
+  uint32_t idx_k_bytes, idx_v_bytes;
+} qwm_layout_info;
+
+/* Host handle of one compressed cache.  Fill with qwm_cache_init. */
+typedef struct qwm_cache {
+  void* base;          /* device, layout.cache_bytes */
+  const void* calib;   /* device, layout.calib_bytes */
+  int64_t n_k;         /* Keys appended so far (tokens) */
+  int64_t n_v;         /* Values appended so far (tokens) */
+  int32_t abi_version;
+  int32_t reserved;
+} qwm_cache;
+
+int32_t qwm_abi_version(void);
+
+/* Text for a status code (thread-local detail for QWM_ERR_HIP).  Never NULL. */
+const char* qwm_status_string(int status);
+
+/* Validates cfg and fills the block sizes and offsets (host out).  No HIP call. */
+int qwm_layout(const qwm_config* cfg, qwm_layout_info* out);
+
+/*
+ * Compression accounting of n_tokens cached tokens ([digest], systems
+ * paragraph; [review] FAQ: the ratio counts centres, quantization parameters
+ * and compensation data).  stored_bytes (host out) counts the format's own
+ * fields: indices, codes, tile parameters, INT8 coefficients and their scales,
+ * the centres, U and s.  resident_bytes (host out, nullable) adds the derived
+ * calibration fields and alignment that the library keeps resident.
+ * original_bytes (host out) is 2*n_tokens*H*d*sizeof(io).  No HIP call.
+ */
+int qwm_footprint(const qwm_config* cfg, int64_t n_tokens, uint64_t* stored_bytes,
+                  uint64_t* resident_bytes, uint64_t* original_bytes);
+
+/*
+ * Calibration on the host (all pointers host).  From historical Queries only
+ * ([digest]: both designs use Query statistics of already-generated content;
+ * [review] Eq. 7: E[(q^T e)^2] = e^T M e):
+ *   M = (1/n_q) sum q q^T (uncentred, fp64); sens = diag(M);
+ *   u = eigenvectors of the r largest eigenvalues of M, descending, each
+ *       column's largest-magnitude entry positive (cyclic Jacobi, fp64);
+ *   energy[h] = sum of the r largest eigenvalues / trace(M)
+ *       ([digest], PSAC paragraph: top-8 directions hold about 71 %);
+ *   mu_k, mu_v = Lloyd k-means of k_hist / v_hist (fp64, kmeans_iters rounds,
+ *       Forgy start from a SplitMix64 partial Fisher-Yates shuffle seeded with
+ *       seed + 2h for Keys and seed + 2h + 1 for Values, ties to the lowest
+ *       index, empty clusters keep their centre), stored rounded to the io
+ *       precision (bf16 round-to-nearest-even, or fp32).
+ * Inputs are contiguous fp32 arrays [H][n][d] holding io-precision values;
+ * outputs are fp32 arrays mu_k [H][C_K][d], mu_v [H][C_V][d], sens [H][d],
+ * u [H][d][r], and energy fp64 [H] (nullable).  Requires n_kv >= max(C_K, C_V)
+ * and n_q >= 1.  Deterministic; multi-threaded over heads.
+ */
+int qwm_calibrate_host(const qwm_config* cfg, const float* q_hist, int64_t n_q,
+                       const float* k_hist, const float* v_hist, int64_t n_kv,
+                       uint64_t seed, int32_t kmeans_iters, float* mu_k, float* mu_v,
+                       float* sens, float* u, double* energy);
+
+/*
+ * Loads a calibration (host fp32 arrays in the shapes of qwm_calibrate_host's
+ * outputs; mu values must be exact in the io precision) into the device
+ * calibration block and computes its derived fields.  Synchronous on stream.
+ */
+int qwm_calib_import(const qwm_config* cfg, void* calib, const float* mu_k,
+                     const float* mu_v, const float* sens, const float* u, void* stream);
+
+/*
+ * Device-side calibration: copies q_hist [H][n_q][d] and k_hist, v_hist
+ * [H][n_kv][d] (io dtype, strided) to the host, runs qwm_calibrate_host and
+ * qwm_calib_import.  energy (host, nullable) receives [H] fp64.  Synchronous.
+ */
+int qwm_calibrate(const qwm_config* cfg, void* calib, const void* q_hist, int64_t n_q,
+                  const qwm_strides* st_q, const void* k_hist, const void* v_hist,
+                  int64_t n_kv, const qwm_strides* st_kv, uint64_t seed,
+                  int32_t kmeans_iters, double* energy, void* stream);
+
+/* Binds an empty cache (n_k = n_v = 0) to a cache block and a calibration
+ * block.  No HIP call; appends overwrite every field they cover. */
+int qwm_cache_init(const qwm_config* cfg, const void* calib, void* base, qwm_cache* cache);
+
+/*
+ * Quantize-append of n_new Keys (whole frames: n_new % F == 0, else
+ * QWM_ERR_ALIGN; beyond capacity: QWM_ERR_CAPACITY) at token cache->n_k.
+ * Per token ([digest] QSAC and PSAC paragraphs; [abstract]):
+ *  QSAC stage 1: D_c = sum_j s_j (k_j - mu_cj)^2 over all C_K centres; keep
+ *     the K_c smallest (ties to the lower index).
+ *  QSAC stage 2: P_c = sum_g S_g range_g(rho)^2 with rho = fl32(k - mu_c) and
+ *     range_g the max - min over the token's 16 channels of group g; choose
+ *     argmin P (ties: smaller D, then lower index).  QWM_NO_RANGE_TERM or
+ *     K_c = 0: argmin D.  QWM_UNIFORM_SENS: s = 1.
+ *  INT2 per 16 channels x T tokens of one frame: z = fp16(min rho),
+ *     s = fp16(fl32(fl32(max - min)/3)); code = #{i in 1..3 : rho >= fl32(z +
+ *     (i - 1/2) s)}; s = 0 gives code 0.
+ *  PSAC: e = k - (mu_c + fl32(z + code s)) in fp64; c = u^T e; c32 = fl32(c);
+ *     sigma = fp16(fl32(max|c32|/127)); coef = clamp(rne(fl32(c32/sigma)),
+ *     -127, 127) (0 when sigma = 0).
+ * Decisions are exact up to score ties of relative size ~1e-15: stage 1 is an
+ * MFMA screen whose error is bounded and whose ambiguous cases are rescored in
+ * fp64; stage 2 and the projection run in fp64.  Advances cache->n_k after
+ * enqueueing.  k_new is [H][n_new][d] in io dtype with strides st.
+ */
+int qwm_quantize_append_k(const qwm_config* cfg, qwm_cache* cache, const void* k_new,
+                          int64_t n_new, const qwm_strides* st, void* stream);
+
+/* Quantize-append of n_new Values: nearest Euclidean centre (ties to the
+ * lower index) and INT2 residual tiles as for Keys, no compensation (the QVG
+ * scheme the method builds on, [digest] QSAC paragraph).  Advances n_v. */
+int qwm_quantize_append_v(const qwm_config* cfg, qwm_cache* cache, const void* v_new,
+                          int64_t n_new, const qwm_strides* st, void* stream);
+
+/* Workspace bytes qwm_attention may use for n_q queries over n_tokens cached
+ * tokens (split-KV partial results).  0 is always accepted by qwm_attention
+ * (then no split is used). */
+size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tokens, int64_t n_q);
+
+/*
+ * Attention of a query chunk q [H][n_q][d] (io dtype) over the compressed
+ * cache (all n_k tokens visible; requires n_k == n_v, else QWM_ERR_STATE):
+ *   k~_t = mu_K[idx_t] + rho_hat_t + u (coef_t * coef_scale_t)
+ *   v~_t = mu_V[idx_t] + rho_hat^V_t
+ *   l_t = scale * q.k~_t  (scale <= 0 selects 1/sqrt(d))
+ *   out = sum_t softmax(l)_t v~_t  [H][n_q][d] io dtype (strides st_out)
+ *   lse = log sum_t exp(l_t)       [H][n_q] fp32 (nullable)
+ * ([abstract]: attention logits QK^T; [digest] PSAC paragraph; [review]: the
+ * compensation is a low-rank correction of the logits).  Keys are rebuilt in
+ * LDS as binary16 and the contractions run on fp16 MFMA with fp32
+ * accumulation.  n_k = 0 gives out = 0 and lse = -inf.  workspace may be NULL
+ * when ws_bytes = 0.
+ */
+int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                  const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
+                  float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* The logits l [H][n_q][n_k] fp32 of the same kernel (debug variant), for
+ * logit parity checks on small shapes. */
+int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, const void* q,
+                         int64_t n_q, const qwm_strides* st_q, float scale, float* logits,
+                         void* stream);
+
+/*
+ * Top-1 token selection ([digest], attention-analysis paragraph: the share of
+ * queries whose highest-scoring historical token changes).  qwm_top1 writes
+ * argmax_t q.k~_t over the compressed cache; qwm_dense_top1 writes argmax_t
+ * q.k_t over original keys k [H][n_k][d] (io dtype).  Both: int32 [H][n_q],
+ * ties to the lowest t, fp32 dot products of the io values.
+ */
+int qwm_top1(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+             const qwm_strides* st_q, int32_t* top1, void* stream);
+int qwm_dense_top1(const qwm_config* cfg, const void* q, int64_t n_q, const qwm_strides* st_q,
+                   const void* k, int64_t n_k, const qwm_strides* st_k, int32_t* top1,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWM_H */

@@ -200,6 +200,7 @@ def psac(k, mu_rows, rho_hat, u):
         return np.zeros((n, 0), np.int8), np.zeros(n, np.float32), np.zeros((n, 0))
     e = np.asarray(k, np.float64) - (np.asarray(mu_rows, np.float64) + np.asarray(rho_hat, np.float64))
     c = e @ np.asarray(u, np.float64)
+    psac.last_abs_scale = np.abs(e) @ np.abs(np.asarray(u, np.float64))
     c32 = fl32(c)
     a = np.max(np.abs(c32), axis=1)
     sigma = fp16_of_f32(fl32(a.astype(np.float64) / 127.0))
@@ -225,8 +226,9 @@ def append_keys(k_new, mu_k, sens, u, frame_tokens, group_tokens, top_k, flags,
     codes, zs, ss, rho_hat = quantize_residuals(
         rho, frame_tokens, group_tokens, bool(flags & FP32_PARAMS_TEST))
     coef, coef_scale, c_exact = psac(k_new, mu_k[idx], rho_hat, u)
+    c_abs = psac.last_abs_scale if u.shape[1] > 0 else np.zeros((k_new.shape[0], 0))
     return dict(idx=idx, codes=codes, z=zs, s=ss, coef=coef, coef_scale=coef_scale,
-                rho=rho, rho_hat=rho_hat, c=c_exact, info=info)
+                rho=rho, rho_hat=rho_hat, c=c_exact, c_abs=c_abs, info=info)
 
 
 def append_values(v_new, mu_v, frame_tokens, group_tokens, idx_override=None):

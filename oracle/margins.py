@@ -11,13 +11,19 @@ downstream before demanding bit-exactness again.
 Kinds
   cand   : |D_(Kc) - D_(Kc+1)| / max    (QSAC candidate-set boundary)
   choice : |P_(1) - P_(2)| / max         (QSAC final choice; D for argmin modes)
-  c32    : distance of c to the nearest binary32 rounding midpoint / |c|
+  c32    : distance of c to the nearest binary32 rounding midpoint, divided by
+           sum_j |U_ji e_j| (the scale of a float64 summation-order error).
+           The projection is float64 on both sides, so c32 is the only PSAC
+           decision that can differ; its tie threshold is PSAC_TIE (1e-12,
+           about 100x the float64 error bound of a 128-term sum).
   sigma  : distance of fl32(a/127) to the nearest binary16 midpoint / sigma
   int8   : |c32/sigma - (n + 1/2)| sigma / a for the nearest half-integer
+           (sigma and int8 are reported only: they are exact functions of c32)
 """
 import numpy as np
 
 TIE = 1e-6
+PSAC_TIE = 1e-12
 
 
 def _rel(a, b):
@@ -54,14 +60,15 @@ def key_margins(info, top_k, flags, no_range_flag=2):
     return dict(cand=cand, choice=choice)
 
 
-def _midpoint_margin_f32(c):
+def _midpoint_dist_f32(c):
+    """Distance of each float64 value to the nearest binary32 rounding midpoint."""
     c = np.asarray(c, np.float64)
     c32 = c.astype(np.float32)
-    nxt = np.nextafter(c32, np.float32(np.inf) * np.sign(c32 + (c32 == 0)))
-    ulp = np.abs(nxt.astype(np.float64) - c32.astype(np.float64))
-    dist = np.abs(np.abs(c - c32.astype(np.float64)) - ulp / 2)
-    with np.errstate(invalid="ignore", divide="ignore"):
-        return np.where(c == 0, np.inf, dist / np.abs(c))
+    up = np.nextafter(c32, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(c32, np.float32(-np.inf)).astype(np.float64)
+    mid_up = (c32.astype(np.float64) + up) / 2
+    mid_dn = (c32.astype(np.float64) + dn) / 2
+    return np.minimum(np.abs(c - mid_up), np.abs(c - mid_dn))
 
 
 def _midpoint_margin_f16(y32):
@@ -74,13 +81,15 @@ def _midpoint_margin_f16(y32):
         return np.where(h == 0, np.inf, dist / np.abs(h.astype(np.float64)))
 
 
-def psac_margins(c_exact, coef_scale):
-    """Per-token minimum margins of the PSAC roundings (c32, sigma, int8)."""
+def psac_margins(c_exact, coef_scale, abs_scale):
+    """Per-token minimum margins of the PSAC roundings (c32, sigma, int8).
+    abs_scale [n, r] = sum_j |U_ji e_j| of each coefficient."""
     n = c_exact.shape[0]
     if c_exact.shape[1] == 0:
         inf = np.full(n, np.inf)
         return dict(c32=inf, sigma=inf, int8=inf)
-    c32m = _midpoint_margin_f32(c_exact).min(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        c32m = np.where(abs_scale > 0, _midpoint_dist_f32(c_exact) / abs_scale, np.inf).min(axis=1)
     c32 = c_exact.astype(np.float32)
     a = np.abs(c32).max(axis=1).astype(np.float64)
     y = (a / 127.0).astype(np.float32)

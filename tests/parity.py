@@ -1,0 +1,149 @@
+"""Helpers shared by the GPU parity tests: run the library on seeded inputs and
+compare against the oracle with tie following.
+
+Tie following: every discrete decision of the oracle carries a float64 margin
+(oracle/margins.py).  Where the library's centre choice differs from the
+oracle's, the margin there must be below 1e-6 (a documented tie); the oracle
+then adopts the library's choice and recomputes everything downstream, and
+the codes, tile parameters and INT8 coefficients must match bit for bit."""
+import numpy as np
+
+import video_world_model_amd as qwm
+import workloads
+from oracle import attention as oa
+from oracle import calibrate as oc
+from oracle import codec, margins
+
+TIE = margins.TIE
+
+
+def cfg_of(w, **kw):
+    c = qwm.Config(heads=w.heads, head_dim=w.head_dim, frame_tokens=w.frame_tokens, max_frames=w.frames,
+                   c_k=w.c_k, c_v=w.c_v, group_tokens=w.group_tokens, top_k=w.top_k, rank=w.rank, io=w.io)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def oracle_calibration(w, data, cfg, seed=7, iters=None):
+    return oc.calibrate(data["q_hist"], data["k_hist"], data["v_hist"], cfg.c_k, cfg.c_v, cfg.rank, cfg.io,
+                        seed=seed, iters=w.kmeans_iters if iters is None else iters)
+
+
+def to_dev(x, cfg):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(cfg.torch_dtype)
+
+
+def build_cache(cfg, cal, k, v, frames_per_call=None):
+    """Import the oracle's calibration, append K and V, return (cache, calib)."""
+    import torch
+    calib = qwm.alloc_calib(cfg)
+    qwm.calib_import(cfg, calib, cal["mu_k"], cal["mu_v"], cal["sens"], cal["u"])
+    cache = qwm.Cache(cfg, calib)
+    kd, vd = to_dev(k, cfg), to_dev(v, cfg)
+    n = k.shape[1]
+    step = n if frames_per_call is None else frames_per_call * cfg.frame_tokens
+    for a in range(0, n, step):
+        qwm.append_k(cache, kd[:, a:a + step])
+        qwm.append_v(cache, vd[:, a:a + step])
+    torch.cuda.synchronize()
+    return cache, calib
+
+
+def gpu_fields(cache, n):
+    """Numpy copies of the cache fields of the first n tokens."""
+    cfg = cache.cfg
+    arr = {k: v.cpu().numpy() for k, v in cache.arrays().items()}
+    tiles = (n // cfg.frame_tokens) * -(-cfg.frame_tokens // cfg.group_tokens)
+    out = {}
+    for kind in ("k", "v"):
+        raw = arr["idx_" + kind][:, :n]
+        if raw.dtype == np.int16:
+            raw = raw.view(np.uint16)
+        out["idx_" + kind] = raw.astype(np.int64)
+        out["codes_" + kind] = arr["codes_" + kind][:, :n].view(np.uint32)
+        pr = arr["params_" + kind][:, :tiles].astype(np.float32)
+        out["z_" + kind], out["s_" + kind] = pr[..., 0], pr[..., 1]
+    if cfg.rank:
+        out["coef"] = arr["coef"][:, :n]
+        out["coef_scale"] = arr["coef_scale"][:, :n].astype(np.float32)
+    return out
+
+
+def bf16_half_ulp(x):
+    """Half the bfloat16 spacing at |x| (8 significant bits)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return np.exp2(e - 8)
+
+
+class Stats(dict):
+    def add(self, key, n):
+        self[key] = self.get(key, 0) + int(n)
+
+
+def check_keys_head(cfg, k, cal, h, gpu, stats):
+    """Tie-following parity of one head's Keys.  Returns the oracle result
+    (with adopted ties) for downstream attention checks."""
+    mu, sens, u = cal["mu_k"][h], cal["sens"][h], cal["u"][h]
+    F, T = cfg.frame_tokens, cfg.group_tokens
+    out = codec.append_keys(k, mu, sens, u, F, T, cfg.top_k, cfg.flags)
+    m = margins.key_margins(out["info"], cfg.top_k, cfg.flags)
+    tie = np.minimum(m["cand"], m["choice"])
+    stats.add("k_decisions", k.shape[0])
+    stats.add("k_flagged_ties", np.sum(tie < TIE))
+    g_idx = gpu["idx_k"][h]
+    mism = np.nonzero(g_idx != out["idx"])[0]
+    bad = [int(t) for t in mism if not tie[t] < TIE]
+    assert not bad, "key centre mismatch outside ties at tokens %s (margins %s)" % (bad[:8], tie[bad[:8]])
+    if len(mism):
+        stats.add("k_adopted", len(mism))
+        out = codec.append_keys(k, mu, sens, u, F, T, cfg.top_k, cfg.flags,
+                                idx_override={int(t): int(g_idx[t]) for t in mism})
+    assert np.array_equal(codec.unpack_codes(gpu["codes_k"][h], cfg.head_dim), out["codes"]), "key codes differ"
+    assert np.array_equal(gpu["z_k"][h], out["z"]), "key zero points differ"
+    assert np.array_equal(gpu["s_k"][h], out["s"]), "key scales differ"
+    if cfg.rank:
+        pm = margins.psac_margins(out["c"], out["coef_scale"], out["c_abs"])
+        ptie = pm["c32"]
+        stats.add("psac_flagged_ties", np.sum(ptie < margins.PSAC_TIE))
+        stats.add("psac_int8_near_half_1e-6", np.sum(pm["int8"] < TIE))
+        diff = np.nonzero(np.any(gpu["coef"][h] != out["coef"], axis=1) | (gpu["coef_scale"][h] != out["coef_scale"]))[0]
+        bad = [int(t) for t in diff if not ptie[t] < margins.PSAC_TIE]
+        assert not bad, "PSAC coefficients differ outside ties at tokens %s" % bad[:8]
+        stats.add("psac_adopted", len(diff))
+        if len(diff):
+            out["coef"] = out["coef"].copy()
+            out["coef_scale"] = out["coef_scale"].copy()
+            out["coef"][diff] = gpu["coef"][h][diff]
+            out["coef_scale"][diff] = gpu["coef_scale"][h][diff]
+    return out
+
+
+def check_values_head(cfg, v, cal, h, gpu, stats):
+    mu = cal["mu_v"][h]
+    F, T = cfg.frame_tokens, cfg.group_tokens
+    out = codec.append_values(v, mu, F, T)
+    tie = margins.argmin_margin(out["info"]["D"])
+    stats.add("v_decisions", v.shape[0])
+    stats.add("v_flagged_ties", np.sum(tie < TIE))
+    g_idx = gpu["idx_v"][h]
+    mism = np.nonzero(g_idx != out["idx"])[0]
+    bad = [int(t) for t in mism if not tie[t] < TIE]
+    assert not bad, "value centre mismatch outside ties at tokens %s" % bad[:8]
+    if len(mism):
+        stats.add("v_adopted", len(mism))
+        out = codec.append_values(v, mu, F, T, idx_override={int(t): int(g_idx[t]) for t in mism})
+    assert np.array_equal(codec.unpack_codes(gpu["codes_v"][h], cfg.head_dim), out["codes"]), "value codes differ"
+    assert np.array_equal(gpu["z_v"][h], out["z"]) and np.array_equal(gpu["s_v"][h], out["s"]), "value params differ"
+    return out
+
+
+def oracle_attention(cfg, cal, h, ko, vo, q, scale=None):
+    kr = oa.reconstruct_keys(ko["idx"], ko["codes"], ko["z"], ko["s"], ko["coef"], ko["coef_scale"],
+                             cal["mu_k"][h], cal["u"][h], cfg.frame_tokens, cfg.group_tokens)
+    vr = oa.reconstruct_values(vo["idx"], vo["codes"], vo["z"], vo["s"], cal["mu_v"][h], cfg.frame_tokens,
+                               cfg.group_tokens)
+    o, lse = oa.softmax_attention(q, kr, vr, scale)
+    return o, lse, kr, vr

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle on seeded
+inputs (tie-following bit-exactness for indices, codes, tile parameters and
+INT8 coefficients; attention outputs within 2e-2 max-abs, lse within 1e-3,
+logits within 1e-3 * tau * ||q|| * ||k~||)."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def case_data(w, heads=None):
+    return workloads.generate(w, heads=heads)
+
+
+CASES = {
+    "tiny": (W["tiny"], {}, 10),
+    "mg_2h_2f": (workloads.scaled(W["matrix_game"], heads=2, frames=2), {}, 3),
+    "lb480_ragged_2h_2f": (workloads.scaled(W["lingbot480p"], heads=2, frames=2), {}, 3),
+    "lb720_1h_1f_c512_k8": (workloads.scaled(W["lingbot720p"], heads=1, frames=1), {}, 2),
+}
+
+
+def run_case(w, overrides, iters, attn=True, logits=False, frames_per_call=None, seed=7, q_rows=None):
+    cfg = P.cfg_of(w, **overrides)
+    say("case %s heads=%d F=%d frames=%d C=%d/%d Kc=%d r=%d T=%d io=%s flags=%d" % (
+        w.name, cfg.heads, cfg.frame_tokens, cfg.max_frames, cfg.c_k, cfg.c_v, cfg.top_k, cfg.rank,
+        cfg.group_tokens, cfg.io, cfg.flags))
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, seed=seed, iters=iters)
+    cache, calib = P.build_cache(cfg, cal, data["k"], data["v"], frames_per_call)
+    n = data["k"].shape[1]
+    assert cache.n_k == n and cache.n_v == n
+    gpu = P.gpu_fields(cache, n)
+    stats = P.Stats()
+    outs = []
+    for h in range(cfg.heads):
+        ko = P.check_keys_head(cfg, data["k"][h], cal, h, gpu, stats)
+        vo = P.check_values_head(cfg, data["v"][h], cal, h, gpu, stats)
+        outs.append((ko, vo))
+    say("  append parity ok: %s" % dict(stats))
+    res = dict(cfg=cfg, data=data, cal=cal, cache=cache, gpu=gpu, outs=outs, stats=stats)
+    if attn:
+        import video_world_model_amd as qwm
+        q = P.to_dev(data["q"], cfg)
+        o, lse = qwm.attention(cache, q)
+        o = o.float().cpu().numpy()
+        lse = lse.cpu().numpy()
+        worst_o, worst_l = 0.0, 0.0
+        for h in range(cfg.heads):
+            ko, vo = outs[h]
+            rows = slice(None) if q_rows is None else q_rows
+            qh = data["q"][h][rows]
+            oo, ll, kr, vr = P.oracle_attention(cfg, cal, h, ko, vo, qh)
+            # 2e-2 bounds the computation for channels up to |v~| ~ 41; the fp16
+            # contraction's own bound 2^-11 max_t |v~_tj| takes over above that,
+            # and a bf16 output adds its storage rounding (half an ulp of |o|)
+            half_ulp = 0.0 if cfg.io == "f32" else P.bf16_half_ulp(oo)
+            tol = np.maximum(2e-2, 2.0 ** -11 * np.abs(vr).max(axis=0))[None, :]
+            worst_o = max(worst_o, float(np.max((np.abs(o[h][rows] - oo) - half_ulp) / tol)))
+            # lse is a smooth maximum of the logits: |dlse| <= max_t |dl_t|, so
+            # it inherits the logit bound 1e-3 * tau * ||q|| * max_t ||k~_t||
+            ltol = 1e-3 / np.sqrt(cfg.head_dim) * np.linalg.norm(qh.astype(np.float64), axis=1) * \
+                np.linalg.norm(kr, axis=1).max()
+            worst_l = max(worst_l, float(np.max(np.abs(lse[h][rows] - ll) / ltol)))
+        say("  attention max(|dO| - half ulp)/tol=%.3g max|dlse|/bound=%.3g" % (worst_o, worst_l))
+        assert worst_o <= 1.0 and worst_l <= 1.0
+        res["o"], res["lse"] = o, lse
+    if logits:
+        import video_world_model_amd as qwm
+        q = P.to_dev(data["q"], cfg)
+        lg = qwm.attention_logits(cache, q).cpu().numpy()
+        tau = 1.0 / np.sqrt(cfg.head_dim)
+        worst = 0.0
+        for h in range(cfg.heads):
+            ko, vo = outs[h]
+            _, _, kr, _ = P.oracle_attention(cfg, cal, h, ko, vo, data["q"][h][:1])
+            qq = data["q"][h].astype(np.float64)
+            ref = tau * qq @ kr.T
+            scale = 1e-3 * tau * np.linalg.norm(qq, axis=1)[:, None] * np.linalg.norm(kr, axis=1)[None, :]
+            worst = max(worst, float(np.max(np.abs(lg[h] - ref) / scale)))
+        say("  logits worst |dl| / (1e-3 tau |q||k~|) = %.3g" % worst)
+        assert worst <= 1.0
+        top = qwm.top1(cache, q).cpu().numpy()
+        for h in range(cfg.heads):
+            ko, vo = outs[h]
+            _, _, kr, _ = P.oracle_attention(cfg, cal, h, ko, vo, data["q"][h][:1])
+            qq = data["q"][h].astype(np.float64)
+            lgt = qq @ kr.T
+            best = lgt.max(axis=1)
+            picked = lgt[np.arange(len(qq)), top[h]]
+            tol = 1e-3 * np.linalg.norm(qq, axis=1) * np.linalg.norm(kr, axis=1).max()
+            assert np.all(best - picked <= tol)
+    return res
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity_cases(name):
+    w, ov, iters = CASES[name]
+    run_case(w, ov, iters, logits=name in ("tiny", "mg_2h_2f"))
+
+
+SMALL = workloads.scaled(W["matrix_game"], heads=2, frames=2)
+
+
+@pytest.mark.parametrize("label,ov", [
+    ("qvg_mode", dict(flags=3)),
+    ("no_range", dict(flags=2)),
+    ("uniform_sens", dict(flags=1)),
+    ("rank0", dict(rank=0)),
+    ("rank16", dict(rank=16)),
+    ("rank5", dict(rank=5)),
+    ("T1", dict(group_tokens=1)),
+    ("T4", dict(group_tokens=4)),
+    ("T32", dict(group_tokens=32)),
+    ("C40", dict(c_k=40, c_v=40)),
+    ("C3_lt_Kc", dict(c_k=3, c_v=3)),
+    ("Kc2", dict(top_k=2)),
+    ("Kc8", dict(top_k=8)),
+    ("Kc0", dict(top_k=0)),
+])
+def test_parity_variants(label, ov):
+    run_case(SMALL, ov, iters=3)
+
+
+def test_parity_head_dim_64_bf16():
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=2, head_dim=64, n_outliers=2)
+    run_case(w, {}, iters=3)
+
+
+def test_parity_f32_head_dim_128():
+    w = workloads.scaled(W["matrix_game"], heads=1, frames=2, io="f32")
+    run_case(w, dict(c_k=64, c_v=64), iters=3)
+
+
+def test_frame_by_frame_equals_bulk():
+    import torch
+    w = workloads.scaled(W["lingbot480p"], heads=2, frames=3)
+    cfg = P.cfg_of(w)
+    say("case frame_by_frame_equals_bulk")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    c1, _ = P.build_cache(cfg, cal, data["k"], data["v"])
+    c2, _ = P.build_cache(cfg, cal, data["k"], data["v"], frames_per_call=1)
+    a1, a2 = c1.arrays(), c2.arrays()
+    for key in a1:
+        assert torch.equal(a1[key], a2[key]), key
+
+
+def test_split_kv_matches_single_and_empty_cache():
+    import torch
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["lingbot480p"], heads=2, frames=4)
+    cfg = P.cfg_of(w)
+    say("case split_kv")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    cache, _ = P.build_cache(cfg, cal, data["k"], data["v"])
+    q = P.to_dev(data["q"][:, :200], cfg)
+    assert qwm.workspace_bytes(cfg, cache.n_k, 200) > 0
+    o_split, l_split = qwm.attention(cache, q)
+    o_one, l_one = qwm.attention(cache, q, workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    # different fp32 summation orders may land on either side of a bf16
+    # rounding boundary: allow one bf16 ulp of |o|
+    ref = o_one.float().cpu().numpy()
+    diff = np.abs(o_split.float().cpu().numpy() - ref)
+    assert np.all(diff <= 4 * P.bf16_half_ulp(ref) + 1e-3)
+    assert float((l_split - l_one).abs().max()) <= 1e-4
+    # empty cache: zero output, lse = -inf
+    empty = qwm.Cache(cfg, cache.calib)
+    o0, l0 = qwm.attention(empty, q)
+    assert float(o0.float().abs().max()) == 0.0 and bool(torch.all(torch.isneginf(l0)))

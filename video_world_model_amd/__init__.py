@@ -1,0 +1,321 @@
+"""Python binding of libqwm, the QuantWM 2-bit KV-cache library for MI355X.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels (include/qwm.h is the contract).  PyTorch provides device memory and
+streams.  Importing this module does not need a GPU; calling a device entry
+point without the built library or without a GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqwm.so")
+
+ABI_VERSION = 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGN, ERR_CAPACITY, ERR_STATE, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+BF16, F32 = 0, 1
+UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE = 1, 2, 3
+
+EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint", "qwm_calibrate_host",
+           "qwm_calib_import", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
+           "qwm_quantize_append_v", "qwm_attention_workspace_size", "qwm_attention",
+           "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
+
+
+class QwmConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "abi_version", "num_heads", "head_dim", "frame_tokens", "max_frames", "num_centroids_k",
+        "num_centroids_v", "group_channels", "group_tokens", "top_candidates", "rank", "io_dtype")] + [
+        ("flags", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
+
+
+class QwmStrides(ctypes.Structure):
+    _fields_ = [("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+_LAYOUT_FIELDS = ["calib_bytes", "cache_bytes", "token_capacity", "tile_capacity",
+                  "mu_k", "mu_v", "sens", "u", "u64", "sgroup", "norm_kw", "norm_k", "norm_v", "head_max",
+                  "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]
+
+
+class QwmLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in _LAYOUT_FIELDS] + [
+        ("idx_k_bytes", ctypes.c_uint32), ("idx_v_bytes", ctypes.c_uint32)]
+
+
+class QwmCache(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("calib", ctypes.c_void_p), ("n_k", ctypes.c_int64),
+                ("n_v", ctypes.c_int64), ("abi_version", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class QwmError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__("qwm status %d: %s" % (status, text))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libqwm (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqwm.so is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, U64, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
+        CFG, ST = ctypes.POINTER(QwmConfig), ctypes.POINTER(QwmStrides)
+        sig = {
+            "qwm_abi_version": (I32, []),
+            "qwm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "qwm_layout": (ctypes.c_int, [CFG, ctypes.POINTER(QwmLayout)]),
+            "qwm_footprint": (ctypes.c_int, [CFG, I64, ctypes.POINTER(U64), ctypes.POINTER(U64), ctypes.POINTER(U64)]),
+            "qwm_calibrate_host": (ctypes.c_int, [CFG, P, I64, P, P, I64, U64, I32, P, P, P, P, P]),
+            "qwm_calib_import": (ctypes.c_int, [CFG, P, P, P, P, P, P]),
+            "qwm_calibrate": (ctypes.c_int, [CFG, P, P, I64, ST, P, P, I64, ST, U64, I32, P, P]),
+            "qwm_cache_init": (ctypes.c_int, [CFG, P, P, ctypes.POINTER(QwmCache)]),
+            "qwm_quantize_append_k": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P]),
+            "qwm_quantize_append_v": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P]),
+            "qwm_attention_workspace_size": (ctypes.c_size_t, [CFG, I64, I64]),
+            "qwm_attention": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, ST, P, P,
+                                             ctypes.c_size_t, P]),
+            "qwm_attention_logits": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, P]),
+            "qwm_top1": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P]),
+            "qwm_dense_top1": (ctypes.c_int, [CFG, P, I64, ST, P, I64, ST, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status):
+    if status != OK:
+        raise QwmError(status, lib().qwm_status_string(status).decode())
+
+
+@dataclasses.dataclass
+class Config:
+    heads: int
+    head_dim: int
+    frame_tokens: int
+    max_frames: int
+    c_k: int
+    c_v: int
+    group_tokens: int = 16
+    top_k: int = 4
+    rank: int = 8
+    io: str = "bf16"
+    flags: int = 0
+
+    def c(self) -> QwmConfig:
+        return QwmConfig(ABI_VERSION, self.heads, self.head_dim, self.frame_tokens, self.max_frames,
+                         self.c_k, self.c_v, 16, self.group_tokens, self.top_k, self.rank,
+                         F32 if self.io == "f32" else BF16, self.flags, 0)
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.float32 if self.io == "f32" else torch.bfloat16
+
+
+def layout(cfg: Config) -> dict:
+    out = QwmLayout()
+    c = cfg.c()
+    check(lib().qwm_layout(ctypes.byref(c), ctypes.byref(out)))
+    return {n: int(getattr(out, n)) for n in _LAYOUT_FIELDS + ["idx_k_bytes", "idx_v_bytes"]}
+
+
+def footprint(cfg: Config, n_tokens: int):
+    """(stored, resident, original) bytes of n_tokens cached tokens."""
+    s, r, o = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    c = cfg.c()
+    check(lib().qwm_footprint(ctypes.byref(c), n_tokens, ctypes.byref(s), ctypes.byref(r), ctypes.byref(o)))
+    return s.value, r.value, o.value
+
+
+def _f32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def calibrate_host(cfg: Config, q_hist, k_hist, v_hist, seed: int, iters: int = 10) -> dict:
+    """Host calibration from numpy [H, n, d] arrays (io-precision values)."""
+    q, k, v = _f32(q_hist), _f32(k_hist), _f32(v_hist)
+    H, d = cfg.heads, cfg.head_dim
+    out = dict(mu_k=np.zeros((H, cfg.c_k, d), np.float32), mu_v=np.zeros((H, cfg.c_v, d), np.float32),
+               sens=np.zeros((H, d), np.float32), u=np.zeros((H, d, max(cfg.rank, 1)), np.float32),
+               energy=np.zeros(H, np.float64))
+    c = cfg.c()
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    check(lib().qwm_calibrate_host(ctypes.byref(c), ptr(q), q.shape[1], ptr(k), ptr(v), k.shape[1], seed, iters,
+                                   ptr(out["mu_k"]), ptr(out["mu_v"]), ptr(out["sens"]), ptr(out["u"]),
+                                   ptr(out["energy"])))
+    out["u"] = out["u"][:, :, :cfg.rank].copy()
+    return out
+
+
+# ------------------------------------------------------------------ device side
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("qwm device entry points need a GPU")
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def strides(t) -> QwmStrides:
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("expected a [heads, tokens, head_dim] tensor with contiguous head_dim")
+    return QwmStrides(t.stride(0), t.stride(1))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def alloc_calib(cfg: Config, device="cuda"):
+    torch = _torch()
+    return torch.empty(layout(cfg)["calib_bytes"], dtype=torch.uint8, device=device)
+
+
+def calib_import(cfg: Config, calib, mu_k, mu_v, sens, u):
+    c = cfg.c()
+    arrs = [_f32(mu_k), _f32(mu_v), _f32(sens), _f32(u if cfg.rank else np.zeros(1))]
+    check(lib().qwm_calib_import(ctypes.byref(c), _ptr(calib), *[a.ctypes.data_as(ctypes.c_void_p) for a in arrs],
+                                 _stream()))
+
+
+def calibrate(cfg: Config, calib, q_hist, k_hist, v_hist, seed: int, iters: int = 10):
+    """Device calibration; returns the per-head energy fraction (numpy)."""
+    c = cfg.c()
+    energy = np.zeros(cfg.heads, np.float64)
+    sq, skv = strides(q_hist), strides(k_hist)
+    check(lib().qwm_calibrate(ctypes.byref(c), _ptr(calib), _ptr(q_hist), q_hist.shape[1], ctypes.byref(sq),
+                              _ptr(k_hist), _ptr(v_hist), k_hist.shape[1], ctypes.byref(skv), seed, iters,
+                              energy.ctypes.data_as(ctypes.c_void_p), _stream()))
+    return energy
+
+
+class Cache:
+    """A compressed cache: owns its device block and the host handle."""
+
+    def __init__(self, cfg: Config, calib, device="cuda"):
+        torch = _torch()
+        self.cfg = cfg
+        self.layout = layout(cfg)
+        self.calib = calib
+        self.base = torch.empty(self.layout["cache_bytes"], dtype=torch.uint8, device=device)
+        self.handle = QwmCache()
+        c = cfg.c()
+        check(lib().qwm_cache_init(ctypes.byref(c), _ptr(calib), _ptr(self.base), ctypes.byref(self.handle)))
+
+    @property
+    def n_k(self):
+        return self.handle.n_k
+
+    @property
+    def n_v(self):
+        return self.handle.n_v
+
+    def arrays(self) -> dict:
+        """Views of the cache fields (per head, full capacity) for inspection."""
+        torch = _torch()
+        L, cfg = self.layout, self.cfg
+        H, N, P, ng, r = cfg.heads, L["token_capacity"], L["tile_capacity"], cfg.head_dim // 16, cfg.rank
+
+        def view(off, count, dtype, shape):
+            nbytes = count * torch.empty(0, dtype=dtype).element_size()
+            return self.base[off:off + nbytes].view(dtype).view(*shape)
+        it = lambda b: torch.uint8 if b == 1 else torch.int16
+        out = dict(
+            idx_k=view(L["idx_k"], H * N, it(L["idx_k_bytes"]), (H, N)),
+            codes_k=view(L["codes_k"], H * N * ng, torch.int32, (H, N, ng)),
+            params_k=view(L["params_k"], H * P * ng * 2, torch.float16, (H, P, ng, 2)),
+            idx_v=view(L["idx_v"], H * N, it(L["idx_v_bytes"]), (H, N)),
+            codes_v=view(L["codes_v"], H * N * ng, torch.int32, (H, N, ng)),
+            params_v=view(L["params_v"], H * P * ng * 2, torch.float16, (H, P, ng, 2)))
+        if r:
+            out["coef"] = view(L["coef"], H * N * r, torch.int8, (H, N, r))
+            out["coef_scale"] = view(L["coef_scale"], H * N, torch.float16, (H, N))
+        return out
+
+
+def append_k(cache: Cache, k):
+    c = cache.cfg.c()
+    s = strides(k)
+    check(lib().qwm_quantize_append_k(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(k), k.shape[1],
+                                      ctypes.byref(s), _stream()))
+
+
+def append_v(cache: Cache, v):
+    c = cache.cfg.c()
+    s = strides(v)
+    check(lib().qwm_quantize_append_v(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(v), v.shape[1],
+                                      ctypes.byref(s), _stream()))
+
+
+def workspace_bytes(cfg: Config, n_tokens: int, n_q: int) -> int:
+    c = cfg.c()
+    return int(lib().qwm_attention_workspace_size(ctypes.byref(c), n_tokens, n_q))
+
+
+def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float = 0.0):
+    torch = _torch()
+    cfg = cache.cfg
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(cfg.heads, q.shape[1], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = workspace_bytes(cfg, cache.n_k, q.shape[1])
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    c = cfg.c()
+    sq, so = strides(q), strides(out)
+    nb = workspace.numel() if workspace is not None else 0
+    check(lib().qwm_attention(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1], ctypes.byref(sq),
+                              scale, _ptr(out), ctypes.byref(so), _ptr(lse), _ptr(workspace), nb, _stream()))
+    return out, lse
+
+
+def attention_logits(cache: Cache, q, scale: float = 0.0):
+    torch = _torch()
+    cfg = cache.cfg
+    lg = torch.empty(cfg.heads, q.shape[1], cache.n_k, dtype=torch.float32, device=q.device)
+    c = cfg.c()
+    sq = strides(q)
+    check(lib().qwm_attention_logits(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1],
+                                     ctypes.byref(sq), scale, _ptr(lg), _stream()))
+    return lg
+
+
+def top1(cache: Cache, q):
+    torch = _torch()
+    cfg = cache.cfg
+    out = torch.empty(cfg.heads, q.shape[1], dtype=torch.int32, device=q.device)
+    c = cfg.c()
+    sq = strides(q)
+    check(lib().qwm_top1(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1], ctypes.byref(sq),
+                         _ptr(out), _stream()))
+    return out
+
+
+def dense_top1(cfg: Config, q, k):
+    torch = _torch()
+    out = torch.empty(cfg.heads, q.shape[1], dtype=torch.int32, device=q.device)
+    c = cfg.c()
+    sq, sk = strides(q), strides(k)
+    check(lib().qwm_dense_top1(ctypes.byref(c), _ptr(q), q.shape[1], ctypes.byref(sq), _ptr(k), k.shape[1],
+                               ctypes.byref(sk), _ptr(out), _stream()))
+    return out

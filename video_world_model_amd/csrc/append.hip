@@ -1,0 +1,24 @@
+// Dispatch of the quantize-append kernels (see append_impl.h).
+#include "qwm_internal.h"
+
+namespace qwm {
+
+hipError_t launch_append_d64_bf16(const AppendParams& p, int heads, bool key, hipStream_t stream);
+hipError_t launch_append_d64_f32(const AppendParams& p, int heads, bool key, hipStream_t stream);
+hipError_t launch_append_d128_bf16(const AppendParams& p, int heads, bool key, hipStream_t stream);
+hipError_t launch_append_d128_f32(const AppendParams& p, int heads, bool key, hipStream_t stream);
+
+size_t append_lds_bytes(int Cpad, int head_dim, bool f32io) {
+  const size_t row = (size_t)(head_dim + 8) * 2;
+  return (size_t)Cpad * row * (f32io ? 2 : 1) + (size_t)Cpad * 4 + (size_t)head_dim * 4;
+}
+
+hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io, bool key,
+                         hipStream_t stream) {
+  if (p.total_segs == 0) return hipSuccess;
+  if (head_dim == 128) return f32io ? launch_append_d128_f32(p, heads, key, stream)
+                                    : launch_append_d128_bf16(p, heads, key, stream);
+  return f32io ? launch_append_d64_f32(p, heads, key, stream) : launch_append_d64_bf16(p, heads, key, stream);
+}
+
+}  // namespace qwm

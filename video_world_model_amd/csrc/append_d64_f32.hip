@@ -1,0 +1,8 @@
+// Append kernels instantiated for head_dim 64, f32 activations.
+#include "append_impl.h"
+
+namespace qwm {
+hipError_t launch_append_d64_f32(const AppendParams& p, int heads, bool key, hipStream_t stream) {
+  return append_detail::dispatch_d<64, true>(p, heads, key, stream);
+}
+}  // namespace qwm

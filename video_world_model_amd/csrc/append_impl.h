@@ -1,0 +1,494 @@
+// Quantize-append kernels for gfx950 (CDNA4): QSAC centre choice, INT2 residual
+// tiles and PSAC INT8 compensation for Keys; nearest centre + INT2 for Values.
+//
+// Method: QuantWM ([digest] "Flickering after quantization? A temporally stable
+// 2-bit KV Cache compression framework for video world models emerges", QSAC
+// and PSAC paragraphs; [review] summary, Eq. 7).  The arithmetic of every
+// stored field is the one documented for qwm_quantize_append_k in qwm.h.
+//
+// Work decomposition.  A workgroup (4 waves) serves one head and 8 segments
+// of <= 32 tokens; each segment is a 32-token MFMA N-block.  The head's
+// centre codebook is staged once in LDS (bf16, rows padded by 16 bytes).
+//
+//  1. Screen (MFMA, bf16 -> fp32): F_c = x . mu_c - ||mu_c||_s^2 / 2 for all c,
+//     x = s * k split into bf16 hi + lo (Values: x = v, exact in bf16), so
+//     argmax F = argmin D.  A = 32 centres x 16 channels from LDS, B = 32
+//     tokens x 16 channels from registers; the accumulator starts at
+//     -||mu||_s^2/2.  Lane (t, h) ends with token t's scores of 16 centres per
+//     block; it keeps the top K_c + 1 as float keys whose low bits carry the
+//     centre index (one max + K_c med3 per score), then merges with lane t^32.
+//  2. Certification: |F~ - F| <= eps (bound below).  If the K_c-th and
+//     (K_c+1)-th keys differ by more than 2 eps the candidate set is exact;
+//     otherwise the lane rescores all centres in fp64 (rare).
+//  3. Lane = token from here.  QSAC stage 2 scores each candidate's residual
+//     ranges in fp64; the INT2 tile min/max is a butterfly over the T lanes of
+//     a tile; PSAC accumulates c = U^T e in fp64 with U read wave-uniformly.
+#pragma once
+#include "qwm_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace qwm {
+namespace append_detail {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPad = 8;  // bf16 elements of padding per LDS codebook row
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t to_half_bits(float x) {
+  return __half_as_ushort(__float2half_rn(x));
+}
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+
+// Insert a key into a descending list of L keys (keeps the L largest).
+template <int L>
+__device__ __forceinline__ void topl_insert(float (&l)[L], float x) {
+#pragma unroll
+  for (int i = L - 1; i >= 1; --i) l[i] = __builtin_amdgcn_fmed3f(l[i - 1], l[i], x);
+  l[0] = fmaxf(l[0], x);
+}
+
+// Eight consecutive io-typed values of a row, as floats.
+template <bool F32IO>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
+  if constexpr (F32IO) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+    v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+  }
+}
+
+// Candidate-count buckets compiled: 1 (argmin modes), 4, 8.
+template <int D, bool F32IO, bool KEY, int KC, int R>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NG = D / 16;      // residual groups (= MFMA k-steps of 16 channels)
+  constexpr int ROW = D + kPad;   // LDS row pitch (bf16 elements)
+  constexpr int L = KC + 1;       // tracked keys
+  constexpr int NV = D / 8;       // 8-value chunks per row
+
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int C = p.C;
+  const int Cpad = p.Cpad;
+
+  __bf16* mu_hi = reinterpret_cast<__bf16*>(smem);
+  __bf16* mu_lo = mu_hi + Cpad * ROW;  // used for fp32 activations only
+  float* init = reinterpret_cast<float*>(mu_hi + Cpad * ROW * (F32IO ? 2 : 1));
+  float* s_lds = init + Cpad;
+
+  const void* mu_g = F32IO ? static_cast<const void*>(static_cast<const float*>(p.mu) + (int64_t)h * C * D)
+                           : static_cast<const void*>(static_cast<const uint16_t*>(p.mu) + (int64_t)h * C * D);
+
+  // ---- stage the codebook, the accumulator start values and s in LDS ----
+  for (int e = threadIdx.x; e < Cpad * NV; e += 256) {
+    const int c = e / NV, j8 = (e % NV) * 8;
+    if constexpr (F32IO) {
+      float v[8];
+      if (c < C) load8<true>(mu_g, (int64_t)c * D + j8, v);
+      else for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      bf16x8 hi, lo;
+      for (int i = 0; i < 8; ++i) {
+        hi[i] = (__bf16)v[i];
+        lo[i] = (__bf16)(v[i] - (float)hi[i]);
+      }
+      *reinterpret_cast<bf16x8*>(mu_hi + c * ROW + j8) = hi;
+      *reinterpret_cast<bf16x8*>(mu_lo + c * ROW + j8) = lo;
+    } else {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (c < C) w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(mu_g) + (int64_t)c * D + j8);
+      *reinterpret_cast<uint4*>(mu_hi + c * ROW + j8) = w;
+    }
+  }
+  for (int c = threadIdx.x; c < Cpad; c += 256)
+    init[c] = c < C ? -p.norm_half[(int64_t)h * C + c] : -3.0e38f;
+  for (int j = threadIdx.x; j < D; j += 256)
+    s_lds[j] = p.uniform ? 1.f : p.sens[(int64_t)h * D + j];
+  __syncthreads();
+
+  // ---- segments of this wave ----
+  const int seg_base = (blockIdx.x * kAppendWaves + wave) * kSegsPerWave;
+  int seg_len[kSegsPerWave], seg_first[kSegsPerWave], seg_pos[kSegsPerWave], seg_frame[kSegsPerWave];
+#pragma unroll
+  for (int s = 0; s < kSegsPerWave; ++s) {
+    const int g = seg_base + s;
+    if (g < p.total_segs) {
+      const int fr = g / p.segs_per_frame, sif = g % p.segs_per_frame;
+      seg_frame[s] = fr;
+      seg_pos[s] = sif * kSegTokens;
+      seg_first[s] = fr * p.F + sif * kSegTokens;
+      seg_len[s] = min(kSegTokens, p.F - sif * kSegTokens);
+    } else {
+      seg_frame[s] = 0; seg_pos[s] = 0; seg_first[s] = 0; seg_len[s] = 0;
+    }
+  }
+  if (seg_len[0] == 0) return;  // wave-uniform; no workgroup barrier follows
+
+  const void* xin = F32IO ? static_cast<const void*>(static_cast<const float*>(p.x) + (int64_t)h * p.head_stride)
+                          : static_cast<const void*>(static_cast<const uint16_t*>(p.x) + (int64_t)h * p.head_stride);
+
+  // ---- 1. screen ----
+  constexpr bool kLo = KEY || F32IO;  // x needs a bf16 lo part
+  bf16x8 xh[kSegsPerWave][NG];
+  bf16x8 xl[kSegsPerWave][kLo ? NG : 1];
+  float ksq[kSegsPerWave];
+#pragma unroll
+  for (int s = 0; s < kSegsPerWave; ++s) {
+    const bool valid = l32 < seg_len[s];
+    const int64_t row = (int64_t)(seg_first[s] + (valid ? l32 : 0)) * p.token_stride;
+    ksq[s] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NG; ++ks) {
+      const int c0 = 16 * ks + 8 * half;
+      float v[8];
+      if (valid) load8<F32IO>(xin, row + c0, v);
+      else for (int i = 0; i < 8; ++i) v[i] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xf = KEY ? s_lds[c0 + i] * v[i] : v[i];
+        ksq[s] = fmaf(xf, v[i], ksq[s]);
+        const __bf16 hb = (__bf16)xf;
+        xh[s][ks][i] = hb;
+        if constexpr (kLo) xl[s][ks][i] = (__bf16)(xf - (float)hb);
+      }
+    }
+  }
+
+  const uint32_t pb = 32 - __builtin_clz((uint32_t)(Cpad - 1));
+  const uint32_t mask = (1u << pb) - 1u;
+  float lst[kSegsPerWave][L];
+#pragma unroll
+  for (int s = 0; s < kSegsPerWave; ++s)
+#pragma unroll
+    for (int i = 0; i < L; ++i) lst[s][i] = -INFINITY;
+
+  for (int blk = 0; blk < Cpad / 32; ++blk) {
+    f32x16 acc[kSegsPerWave];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = init[blk * 32 + 8 * (i / 4) + 4 * half + (i % 4)];
+#pragma unroll
+      for (int s = 0; s < kSegsPerWave; ++s) acc[s][i] = v;
+    }
+    const __bf16* arow = mu_hi + (blk * 32 + l32) * ROW + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < NG; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
+#pragma unroll
+      for (int s = 0; s < kSegsPerWave; ++s) {
+        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xh[s][ks], acc[s], 0, 0, 0);
+        if constexpr (kLo) acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xl[s][ks], acc[s], 0, 0, 0);
+      }
+      if constexpr (F32IO) {
+        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(mu_lo + (blk * 32 + l32) * ROW + 8 * half + 16 * ks);
+#pragma unroll
+        for (int s = 0; s < kSegsPerWave; ++s)
+          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, xh[s][ks], acc[s], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = (uint32_t)(blk * 32 + 8 * (i / 4) + 4 * half + (i % 4));
+#pragma unroll
+      for (int s = 0; s < kSegsPerWave; ++s) {
+        const float key = __uint_as_float((__float_as_uint(acc[s][i]) & ~mask) | c);
+        topl_insert<L>(lst[s], key);
+      }
+    }
+  }
+
+  // merge the two half-lists of each token (lanes t and t^32)
+#pragma unroll
+  for (int s = 0; s < kSegsPerWave; ++s) {
+    float other[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) other[i] = __shfl_xor(lst[s][i], 32);
+#pragma unroll
+    for (int i = 0; i < L; ++i) topl_insert<L>(lst[s], other[i]);
+    ksq[s] += __shfl_xor(ksq[s], 32);
+  }
+
+  // ---- 2. certification ----
+  // |F~_c - F_c| <= eps = c1 (A + 1.01 ||x||_s maxnorm), A = maxnorm^2 / 2, with
+  // c1 = 2^-12 covering: fp32 accumulation of <= 3d+1 terms (4 (3d+2) 2^-24),
+  // the bf16 hi/lo split of x and mu (<= 2^-16), the norm's rounding (2^-24)
+  // and the key's index bits (2^(pb-23) <= 2^-14 for C <= 512).
+  const float mx = p.head_max[h * 4 + p.head_max_slot];
+  const int kc = p.Kc;
+  const int sidx = half;  // lane = token from here: segment `half`, token l32
+  float mylst[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) mylst[i] = sidx ? lst[1][i] : lst[0][i];
+  const float myksq = sidx ? ksq[1] : ksq[0];
+  const float eps = 0x1p-12f * (0.5f * mx * mx + 1.01f * sqrtf(myksq) * mx) + 1e-30f;
+  float th = mylst[0], ph = mylst[1];
+#pragma unroll
+  for (int i = 1; i < L; ++i) {
+    if (i == kc - 1) th = mylst[i];
+    if (i == kc) ph = mylst[i];
+  }
+  const bool certain = (C <= kc) || (th - ph > 2.f * eps);
+
+  const int mylen = sidx ? seg_len[1] : seg_len[0];
+  const bool valid = l32 < mylen;
+  const int first = sidx ? seg_first[1] : seg_first[0];
+  const int pos = (sidx ? seg_pos[1] : seg_pos[0]) + l32;  // token position inside its frame
+  const int frame = p.frame0 + (sidx ? seg_frame[1] : seg_frame[0]);
+  const int tok_rel = first + (valid ? l32 : 0);
+  const int64_t tok = p.tok0 + tok_rel;
+
+  // ---- 3. lane = token: the token's row in registers ----
+  float kv[D];
+  {
+    const int64_t row = (int64_t)tok_rel * p.token_stride;
+#pragma unroll
+    for (int j8 = 0; j8 < NV; ++j8) {
+      float v[8];
+      load8<F32IO>(xin, row + 8 * j8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kv[8 * j8 + i] = valid ? v[i] : 0.f;
+    }
+  }
+
+  int cand[KC];
+  float tieD[KC];  // smaller is better; approximate (-key) or exact D
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    // clamp: only non-finite inputs can produce an index outside [0, C)
+    cand[i] = min((int)(__float_as_uint(mylst[i]) & mask), C - 1);
+    tieD[i] = -mylst[i];
+  }
+
+  if (!certain && valid) {
+    // exact fp64 rescoring of every centre: ascending (D, c)
+    double bd[KC];
+    int bc[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) { bd[i] = INFINITY; bc[i] = 0; }
+    for (int c = 0; c < C; ++c) {
+      double dd = 0.0;
+#pragma unroll
+      for (int j8 = 0; j8 < NV; ++j8) {
+        float m8[8];
+        if constexpr (F32IO) load8<true>(mu_g, (int64_t)c * D + 8 * j8, m8);
+        else {
+          uint4 w = *reinterpret_cast<const uint4*>(mu_hi + c * ROW + 8 * j8);
+          m8[0] = bf_lo(w.x); m8[1] = bf_hi(w.x); m8[2] = bf_lo(w.y); m8[3] = bf_hi(w.y);
+          m8[4] = bf_lo(w.z); m8[5] = bf_hi(w.z); m8[6] = bf_lo(w.w); m8[7] = bf_hi(w.w);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double df = (double)kv[8 * j8 + i] - (double)m8[i];
+          dd = fma((double)s_lds[8 * j8 + i] * df, df, dd);
+        }
+      }
+      // sorted insertion; equal D keeps the earlier (lower) c first
+#pragma unroll
+      for (int i = KC - 1; i >= 1; --i) {
+        if (dd < bd[i - 1]) { bd[i] = bd[i - 1]; bc[i] = bc[i - 1]; }
+        else if (dd < bd[i]) { bd[i] = dd; bc[i] = c; }
+      }
+      if (dd < bd[0]) { bd[0] = dd; bc[0] = c; }
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) { cand[i] = bc[i]; tieD[i] = (float)bd[i]; }
+  }
+
+  auto mu_row16 = [&](int c, int g, float (&m)[16]) {
+    float a[8], b[8];
+    if constexpr (F32IO) {
+      load8<true>(mu_g, (int64_t)c * D + 16 * g, a);
+      load8<true>(mu_g, (int64_t)c * D + 16 * g + 8, b);
+    } else {
+      const uint4* q = reinterpret_cast<const uint4*>(mu_hi + c * ROW + 16 * g);
+      uint4 w0 = q[0], w1 = q[1];
+      a[0] = bf_lo(w0.x); a[1] = bf_hi(w0.x); a[2] = bf_lo(w0.y); a[3] = bf_hi(w0.y);
+      a[4] = bf_lo(w0.z); a[5] = bf_hi(w0.z); a[6] = bf_lo(w0.w); a[7] = bf_hi(w0.w);
+      b[0] = bf_lo(w1.x); b[1] = bf_hi(w1.x); b[2] = bf_lo(w1.y); b[3] = bf_hi(w1.y);
+      b[4] = bf_lo(w1.z); b[5] = bf_hi(w1.z); b[6] = bf_lo(w1.w); b[7] = bf_hi(w1.w);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { m[i] = a[i]; m[8 + i] = b[i]; }
+  };
+
+  // ---- QSAC stage 2: expected INT2 logit perturbation of each candidate ----
+  int chosen = cand[0];
+  if constexpr (KEY && KC > 1) {
+    if (p.use_range) {
+      const double* sg = p.sgroup + (int64_t)h * NG;
+      double bestP = INFINITY;
+      float bestD = INFINITY;
+      int best = 0x7fffffff;
+      for (int i = 0; i < kc; ++i) {
+        int c = cand[0];
+        float td = tieD[0];
+#pragma unroll
+        for (int q = 1; q < KC; ++q)
+          if (q == i) { c = cand[q]; td = tieD[q]; }
+        if (c >= C) continue;  // padding rows when C < K_c
+        double P = 0.0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          float m[16];
+          mu_row16(c, g, m);
+          float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float rho = kv[16 * g + j] - m[j];
+            lo = fminf(lo, rho);
+            hi = fmaxf(hi, rho);
+          }
+          const double rg = (double)hi - (double)lo;
+          P = fma(p.uniform ? 16.0 : sg[g], rg * rg, P);
+        }
+        const bool better = (P < bestP) || (P == bestP && (td < bestD || (td == bestD && c < best)));
+        if (better) { bestP = P; bestD = td; best = c; }
+      }
+      chosen = best < C ? best : cand[0];  // all-NaN scores keep a valid index
+    }
+  }
+
+  // ---- INT2 residual tiles and PSAC ----
+  const int T = p.T;
+  const int tile = frame * p.tpf + pos / T;
+  uint32_t words[NG];
+  double cacc[R > 0 ? R : 1];
+#pragma unroll
+  for (int i = 0; i < (R > 0 ? R : 1); ++i) cacc[i] = 0.0;
+  const double* U = p.u64 + (int64_t)h * D * p.rp;
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float m[16];
+    mu_row16(chosen, g, m);
+    float rho[16];
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      rho[j] = kv[16 * g + j] - m[j];
+      lo = fminf(lo, rho[j]);
+      hi = fmaxf(hi, rho[j]);
+    }
+    if (!valid) { lo = INFINITY; hi = -INFINITY; }
+    for (int off = 1; off < T; off <<= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off));
+      hi = fmaxf(hi, __shfl_xor(hi, off));
+    }
+    const uint16_t zb = to_half_bits(lo);
+    const uint16_t sb = to_half_bits((hi - lo) / 3.0f);
+    const float zf = half_bits_to_float(zb);
+    const float sf = half_bits_to_float(sb);
+    const float t1 = zf + 0.5f * sf, t2 = zf + 1.5f * sf, t3 = zf + 2.5f * sf;
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t code = 0;
+      if (sf != 0.f) code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
+      w |= code << (2 * j);
+      if constexpr (KEY && R > 0) {
+        const float rhat = fmaf((float)code, sf, zf);
+        const double e = ((double)kv[16 * g + j] - (double)m[j]) - (double)rhat;
+        const double* urow = U + (int64_t)(16 * g + j) * p.rp;
+#pragma unroll
+        for (int i = 0; i < R; ++i) cacc[i] = fma(urow[i], e, cacc[i]);
+      }
+    }
+    words[g] = w;
+    if (valid && (pos % T) == 0)
+      p.params[((int64_t)h * p.Pcap + tile) * NG + g] = (uint32_t)zb | ((uint32_t)sb << 16);
+  }
+
+  if (!valid) return;
+  const int64_t slot = (int64_t)h * p.Ncap + tok;
+  if (p.idx_bytes == 1) static_cast<uint8_t*>(p.idx)[slot] = (uint8_t)chosen;
+  else static_cast<uint16_t*>(p.idx)[slot] = (uint16_t)chosen;
+  uint4* cw = reinterpret_cast<uint4*>(p.codes + slot * NG);
+#pragma unroll
+  for (int q = 0; q < NG / 4; ++q) cw[q] = make_uint4(words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
+
+  if constexpr (KEY && R > 0) {
+    const int r = p.r;
+    float c32[R];
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      c32[i] = (float)cacc[i];
+      if (i < r) a = fmaxf(a, fabsf(c32[i]));
+    }
+    const uint16_t sgb = to_half_bits(a / 127.0f);
+    const float sg = half_bits_to_float(sgb);
+    int8_t n[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float v = 0.f;
+      if (sg != 0.f) v = fminf(127.f, fmaxf(-127.f, rintf(c32[i] / sg)));
+      n[i] = (int8_t)(int)v;
+    }
+    int8_t* dst = p.coef + slot * r;
+    if (r == R) {
+      if constexpr (R == 8) {
+        uint2 pk;
+        pk.x = (uint32_t)(uint8_t)n[0] | ((uint32_t)(uint8_t)n[1] << 8) | ((uint32_t)(uint8_t)n[2] << 16) | ((uint32_t)(uint8_t)n[3] << 24);
+        pk.y = (uint32_t)(uint8_t)n[4] | ((uint32_t)(uint8_t)n[5] << 8) | ((uint32_t)(uint8_t)n[6] << 16) | ((uint32_t)(uint8_t)n[7] << 24);
+        *reinterpret_cast<uint2*>(dst) = pk;
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) dst[i] = n[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        if (i < r) dst[i] = n[i];
+    }
+    p.coef_scale[slot] = sgb;
+  }
+}
+
+template <int D, bool F32IO, bool KEY, int KC, int R>
+hipError_t launch_one(const AppendParams& p, int heads, hipStream_t stream) {
+  const size_t lds = append_lds_bytes(p.Cpad, D, F32IO);
+  auto fn = append_kernel<D, F32IO, KEY, KC, R>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((p.total_segs + kSegsPerBlock - 1) / kSegsPerBlock, heads);
+  hipLaunchKernelGGL(fn, grid, dim3(256), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool F32IO>
+inline hipError_t dispatch_d(const AppendParams& p, int heads, bool key, hipStream_t stream) {
+  if (!key) return launch_one<D, F32IO, false, 1, 0>(p, heads, stream);
+  const bool argmin = !p.use_range || p.Kc <= 1;
+  const int rb = p.r == 0 ? 0 : (p.r <= 8 ? 8 : 16);
+  if (argmin) {
+    if (rb == 0) return launch_one<D, F32IO, true, 1, 0>(p, heads, stream);
+    if (rb == 8) return launch_one<D, F32IO, true, 1, 8>(p, heads, stream);
+    return launch_one<D, F32IO, true, 1, 16>(p, heads, stream);
+  }
+  if (p.Kc <= 4) {
+    if (rb == 0) return launch_one<D, F32IO, true, 4, 0>(p, heads, stream);
+    if (rb == 8) return launch_one<D, F32IO, true, 4, 8>(p, heads, stream);
+    return launch_one<D, F32IO, true, 4, 16>(p, heads, stream);
+  }
+  if (rb == 0) return launch_one<D, F32IO, true, 8, 0>(p, heads, stream);
+  if (rb == 8) return launch_one<D, F32IO, true, 8, 8>(p, heads, stream);
+  return launch_one<D, F32IO, true, 8, 16>(p, heads, stream);
+}
+
+}  // namespace append_detail
+}  // namespace qwm

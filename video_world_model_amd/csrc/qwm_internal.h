@@ -1,0 +1,100 @@
+// Internal declarations shared by the host library and the HIP kernels.
+// Not part of the public ABI (include/qwm.h); symbols are hidden.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define QWM_HIDDEN __attribute__((visibility("hidden")))
+
+namespace qwm {
+
+// Tokens of one segment: a run of at most 32 tokens of one frame, starting at
+// a multiple of 32 inside the frame.  Parameter tiles (T | 32) never straddle
+// a segment.
+constexpr int kSegTokens = 32;
+constexpr int kAppendWaves = 4;          // waves per workgroup
+constexpr int kSegsPerWave = 2;          // one 32-token MFMA N-block each
+constexpr int kSegsPerBlock = kAppendWaves * kSegsPerWave;
+
+struct AppendParams {
+  // input activations [H][n_new][d]
+  const void* x;
+  int64_t head_stride, token_stride;  // elements
+  int n_new;
+  int frame0;          // global frame index of the first appended frame
+  int F, T, tpf;       // frame tokens, group tokens, tiles per frame
+  int segs_per_frame;  // ceil(F / 32)
+  int total_segs;      // (n_new / F) * segs_per_frame
+  int C, Cpad;         // centres (padded to a multiple of 32)
+  int Kc;              // tracked candidates: K_c for QSAC, 1 for argmin modes
+  int use_range;       // QSAC stage 2 active
+  int uniform;         // s = 1
+  int r;               // PSAC rank (Keys); 0 for Values
+  int64_t Ncap, Pcap;  // token / tile capacity per head
+  // calibration (per-head arrays; the kernel adds the head offset)
+  const void* mu;         // [H][C][d] io dtype
+  const float* sens;      // [H][d]
+  const double* u64;      // [H][d][RP] zero-padded
+  int rp;                 // RP (row pitch of u64)
+  const double* sgroup;   // [H][d/16]
+  const float* norm_half; // [H][C]  ||mu||^2/2 (weighted or not)
+  const float* head_max;  // [H][4]
+  int head_max_slot;
+  // outputs (cache arrays, base of head 0)
+  void* idx;
+  int idx_bytes;
+  uint32_t* codes;   // [H][Ncap][d/16]
+  uint32_t* params;  // [H][Pcap][d/16] half2
+  int8_t* coef;      // [H][Ncap][r]
+  uint16_t* coef_scale;  // [H][Ncap] fp16 bits
+  int64_t tok0;      // first cache token index of this append
+};
+
+// Attention over the compressed cache.
+struct AttnParams {
+  const void* q;
+  int64_t q_head_stride, q_token_stride;
+  int n_q;
+  int n_k;
+  int F, T, tpf;
+  int r, rp;
+  float scale_log2;  // softmax scale * log2(e)
+  float scale;       // softmax scale
+  int64_t Ncap, Pcap;
+  int C_k, C_v;
+  const void* mu_k;   // [H][C_K][d]
+  const void* mu_v;   // [H][C_V][d]
+  const float* u;     // [H][d][r] fp32
+  const void* idx_k; int idx_k_bytes;
+  const uint32_t* codes_k;
+  const uint32_t* params_k;
+  const int8_t* coef;
+  const uint16_t* coef_scale;
+  const void* idx_v; int idx_v_bytes;
+  const uint32_t* codes_v;
+  const uint32_t* params_v;
+  // outputs
+  void* out;
+  int64_t o_head_stride, o_token_stride;
+  float* lse;            // [H][n_q] or null
+  float* logits;         // debug [H][n_q][n_k] or null
+  int* top1;             // measure [H][n_q] or null
+  // split-KV partials
+  int splits;            // number of key ranges
+  int keys_per_split;    // multiple of the key tile
+  float* part_o;         // [splits][H][n_q][d]
+  float* part_ml;        // [splits][H][n_q][2] (max in log2 units, sum)
+};
+
+QWM_HIDDEN hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io,
+                                    bool key, hipStream_t stream);
+QWM_HIDDEN hipError_t launch_attention(const AttnParams& p, int heads, int head_dim, bool f32io,
+                                       hipStream_t stream);
+QWM_HIDDEN hipError_t launch_dense_top1(const void* q, int64_t qhs, int64_t qts, int n_q,
+                                        const void* k, int64_t khs, int64_t kts, int n_k,
+                                        int heads, int head_dim, bool f32io, int* top1,
+                                        hipStream_t stream);
+QWM_HIDDEN size_t append_lds_bytes(int Cpad, int head_dim, bool f32io);
+
+}  // namespace qwm
