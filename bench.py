@@ -1,0 +1,301 @@
+"""Benchmark of the QuantWM hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input that stays
+resident in HBM: quantize-append of every cached frame's Keys and Values
+(QSAC + INT2 + PSAC for Keys, centre + INT2 for Values) into a fresh cache,
+then attention of the query chunk over the compressed cache.  Calibration (the
+statistics and centres) is done once, untimed, through the library.
+
+`value` is the step throughput in Ktokens/s: cached tokens (all heads) taken
+through append and attention per second.  The line also carries the append
+rate, the attention TFLOP/s, the roofline object of the dominant kernel
+(attention, fp16 MFMA) and the oracle's CPU baseline on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--config matrix_game|lingbot480p|lingbot720p|minute|tiny]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Ktokens/s quantize-append + dequant-attn TFLOP/s, % of HBM/MFMA roofline"
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="matrix_game")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0: auto)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter scaling for profiles)")
+    ap.add_argument("--seed", type=int, default=7)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "video_world_model_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def append_bytes_per_token_head(w, cfg):
+    """Algorithmic HBM bytes of append per token-head (K+V): inputs read once
+    plus the compressed fields written."""
+    b_in = 4 if w.io == "f32" else 2
+    ng = w.head_dim // 16
+    tpf = -(-w.frame_tokens // w.group_tokens)
+    idx = (1 if w.c_k <= 256 else 2) + (1 if w.c_v <= 256 else 2)
+    params = 2 * ng * 4 * tpf / w.frame_tokens
+    coef = (w.rank + 2) if w.rank else 0
+    return 2 * w.head_dim * b_in + idx + 2 * ng * 4 + params + coef
+
+
+def attn_flops(w, n_q, n_k):
+    return 4.0 * n_q * n_k * w.head_dim * w.heads
+
+
+def traffic_from_profiles(config, src_hash):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "attention_%s_traffic.json" % config)
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, data, cfg_host, heads, seed):
+    """The oracle (untuned) on a bounded sample: append + attention of
+    `heads` heads of the same workload, scaled to Ktokens/s of the full step."""
+    import numpy as np
+    from oracle import attention as oa
+    from oracle import calibrate as oc
+    from oracle import codec
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    cal = oc.calibrate(data["q_hist"][:heads], data["k_hist"][:heads], data["v_hist"][:heads],
+                       w.c_k, w.c_v, w.rank, w.io, seed=seed, iters=2)
+    t0 = time.perf_counter()
+    for h in range(heads):
+        ko = codec.append_keys(data["k"][h], cal["mu_k"][h], cal["sens"][h], cal["u"][h], w.frame_tokens,
+                               w.group_tokens, w.top_k, 0)
+        vo = codec.append_values(data["v"][h], cal["mu_v"][h], w.frame_tokens, w.group_tokens)
+        kr = oa.reconstruct_keys(ko["idx"], ko["codes"], ko["z"], ko["s"], ko["coef"], ko["coef_scale"],
+                                 cal["mu_k"][h], cal["u"][h], w.frame_tokens, w.group_tokens)
+        vr = oa.reconstruct_values(vo["idx"], vo["codes"], vo["z"], vo["s"], cal["mu_v"][h], w.frame_tokens,
+                                   w.group_tokens)
+        oa.softmax_attention(data["q"][h], kr, vr)
+    dt = time.perf_counter() - t0
+    step_s = dt * w.heads / heads
+    return {"value": round(w.n_tokens / step_s / 1e3, 4), "unit": "Ktokens/s", "cores": int(min(cores, max(blas, 1))),
+            "kind": "oracle",
+            "sample": "%d of %d heads, all %d cached tokens: oracle append (K+V) + reconstruction attention of %d "
+                      "queries, %.1f s on the host, scaled x%d to the full step; BLAS threads %d, affinity cores %d"
+                      % (heads, w.heads, w.n_tokens, w.n_q, dt, w.heads // heads if w.heads % heads == 0 else 0,
+                         blas, cores)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import video_world_model_amd as qwm
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.WORKLOADS[args.config]
+    cfg = qwm.Config(heads=w.heads, head_dim=w.head_dim, frame_tokens=w.frame_tokens, max_frames=w.frames,
+                     c_k=w.c_k, c_v=w.c_v, group_tokens=w.group_tokens, top_k=w.top_k, rank=w.rank, io=w.io)
+    dt = cfg.torch_dtype
+    t_gen = time.perf_counter()
+    data = workloads.generate(w, threads=16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    k, v, q = dev(data["k"]), dev(data["v"]), dev(data["q"])
+    qh, kh, vh = dev(data["q_hist"]), dev(data["k_hist"]), dev(data["v_hist"])
+    print("[bench] %s: generated in %.1fs" % (w.name, time.perf_counter() - t_gen), file=sys.stderr, flush=True)
+
+    calib = qwm.alloc_calib(cfg)
+    t_cal = time.perf_counter()
+    energy = qwm.calibrate(cfg, calib, qh, kh, vh, seed=args.seed, iters=w.kmeans_iters)
+    print("[bench] calibrated in %.1fs (top-%d energy mean %.3f)" % (time.perf_counter() - t_cal, w.rank,
+          float(energy.mean())), file=sys.stderr, flush=True)
+
+    # rotate input copies over > 512 MiB so the 256 MB MALL cannot serve them
+    in_bytes = 2 * k.numel() * k.element_size()
+    copies = max(1, math.ceil(512 * 2**20 / in_bytes))
+    ks = [k] + [k.clone() for _ in range(copies - 1)]
+    vs = [v] + [v.clone() for _ in range(copies - 1)]
+
+    cache = qwm.Cache(cfg, calib)
+    ws_bytes = qwm.workspace_bytes(cfg, w.n_tokens, w.n_q)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(w.heads, w.n_q, dtype=torch.float32, device="cuda")
+
+    reset = cache.reset
+
+    if args.config == "minute":
+        return rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torch)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(i, e=None):
+        reset()
+        kk, vv = ks[i % copies], vs[i % copies]
+        if e: e[0].record()
+        qwm.append_k(cache, kk)
+        qwm.append_v(cache, vv)
+        if e: e[1].record()
+        if e: e[2].record()
+        qwm.attention(cache, q, out=out, lse=lse, workspace=ws if ws_bytes else None)
+        if e: e[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    app_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    att_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in range(args.steps)]
+    ms_step = wall * 1e3 / args.steps
+    tok_heads = w.n_tokens * w.heads
+    app_bytes = tok_heads * append_bytes_per_token_head(w, cfg)
+    flops = attn_flops(w, w.n_q, w.n_tokens)
+    app_avg, att_avg = float(np.mean(app_ms)), float(np.mean(att_ms))
+    achieved_tf = flops / (att_avg * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles(args.config, src_hash)
+
+    stored, resident, original = qwm.footprint(cfg, w.n_tokens)
+    res = {
+        "metric": METRIC,
+        "value": round(w.n_tokens / (ms_step * 1e-3) / 1e3, 3),
+        "unit": "Ktokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16" if w.io == "bf16" else "f32",
+        "data": "synthetic (seeded workloads module: lognormal-scaled K/V with outlier channels, "
+                "8-direction queries); centres and statistics calibrated by the library",
+        "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim, "frame_tokens": w.frame_tokens,
+                   "cached_frames": w.frames, "cached_tokens": w.n_tokens, "query_chunk": w.n_q,
+                   "centroids_k": w.c_k, "centroids_v": w.c_v, "top_candidates": w.top_k, "rank": w.rank,
+                   "group_tokens": w.group_tokens, "io_dtype": w.io, "parallelism": "single GPU",
+                   "input_copies_rotated": copies},
+        "append": {"ms": round(app_avg, 4), "ktokens_s": round(w.n_tokens / (app_avg * 1e-3) / 1e3, 3),
+                   "token_heads_s": round(tok_heads / (app_avg * 1e-3), 1),
+                   "algorithmic_gbs": round(app_bytes / (app_avg * 1e-3) / 1e9, 2),
+                   "frac_hbm": round(app_bytes / (app_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "bytes_per_token_head": round(append_bytes_per_token_head(w, cfg), 2)},
+        "attention": {"ms": round(att_avg, 4), "tflops": round(achieved_tf, 2),
+                      "frac_mfma": round(achieved_tf / PEAK_FP16_TFLOPS, 4),
+                      "flops_per_launch": flops,
+                      "compressed_cache_gbs": round((stored - 0) / (att_avg * 1e-3) / 1e9, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved_tf / PEAK_FP16_TFLOPS, 4), "traffic": traffic},
+        "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4),
+                        "stored_bytes": stored, "original_bytes": original},
+        "top8_energy_mean": round(float(energy.mean()), 4),
+        "kernel_source_hash": src_hash,
+        "cpu_baseline": None,
+    }
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 2**20 // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = n * 4
+    if not args.no_cpu_baseline:
+        heads = args.cpu_heads or max(1, min(w.heads, {"tiny": 1, "matrix_game": 2}.get(w.name, 1)))
+        res["cpu_baseline"] = cpu_baseline(w, data, cfg, heads, args.seed)
+    print(json.dumps(res), flush=True)
+
+
+def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torch):
+    """1-minute horizon: per generation step append one frame (K and V), then
+    attend the query chunk over everything cached so far."""
+    import numpy as np
+    F = w.frame_tokens
+    reset()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(w.frames)]
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    for f in range(w.frames):
+        e = ev[f]
+        e[0].record()
+        qwm.append_k(cache, ks[0][:, f * F:(f + 1) * F])
+        qwm.append_v(cache, vs[0][:, f * F:(f + 1) * F])
+        e[1].record()
+        qwm.attention(cache, q, out=out, lse=lse, workspace=ws)
+        e[2].record()
+        if f % 40 == 0:
+            print("[bench] rollout frame %d" % f, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    att = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    flops = np.array([attn_flops(w, w.n_q, (f + 1) * F) for f in range(w.frames)])
+    tf = flops / (att * 1e-3) / 1e12
+    stored, resident, original = qwm.footprint(cfg, w.n_tokens)
+    res = {
+        "metric": METRIC, "value": round(w.n_tokens / wall / 1e3, 3), "unit": "Ktokens/s", "n_gpus": 1,
+        "steps": int(w.frames), "warmup": 0, "ms_per_step": round(wall * 1e3 / w.frames, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded workloads module)",
+        "config": {"workload": w.name, "heads": w.heads, "frames": w.frames, "frame_tokens": F,
+                   "query_chunk": w.n_q, "mode": "rollout: append one frame then attend, per step"},
+        "append_ms_median": round(float(np.median(app)), 4),
+        "attention_ms_median": round(float(np.median(att)), 4),
+        "attention_ms_final": round(float(att[-1]), 4),
+        "attention_tflops_final": round(float(tf[-1]), 2),
+        "attention_tflops_steady_median": round(float(np.median(tf[len(tf) // 2:])), 2),
+        "roofline": {"bound": "mfma", "achieved": round(float(tf[-1]), 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(float(tf[-1]) / PEAK_FP16_TFLOPS, 4), "traffic": None},
+        "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

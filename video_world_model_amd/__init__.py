@@ -221,6 +221,11 @@ class Cache:
         c = cfg.c()
         check(lib().qwm_cache_init(ctypes.byref(c), _ptr(calib), _ptr(self.base), ctypes.byref(self.handle)))
 
+    def reset(self):
+        """Empty the cache (counters to zero; the next appends overwrite it)."""
+        c = self.cfg.c()
+        check(lib().qwm_cache_init(ctypes.byref(c), _ptr(self.calib), _ptr(self.base), ctypes.byref(self.handle)))
+
     @property
     def n_k(self):
         return self.handle.n_k

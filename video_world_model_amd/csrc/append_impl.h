@@ -51,7 +51,7 @@ template <int L>
 __device__ __forceinline__ void topl_insert(float (&l)[L], float x) {
 #pragma unroll
   for (int i = L - 1; i >= 1; --i) l[i] = __builtin_amdgcn_fmed3f(l[i - 1], l[i], x);
-  l[0] = fmaxf(l[0], x);
+  l[0] = __builtin_amdgcn_fmed3f(l[0], x, INFINITY);  // max without NaN canonicalisation
 }
 
 // Eight consecutive io-typed values of a row, as floats.
@@ -71,11 +71,11 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)
 
 // Candidate-count buckets compiled: 1 (argmin modes), 4, 8.
 template <int D, bool F32IO, bool KEY, int KC, int R>
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+__global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NG = D / 16;      // residual groups (= MFMA k-steps of 16 channels)
   constexpr int ROW = D + kPad;   // LDS row pitch (bf16 elements)
-  constexpr int L = KC + 1;       // tracked keys
+  constexpr int L = KC + 1 + 3;   // tracked keys: K_c, the next one, and 3 spare for rescoring
   constexpr int NV = D / 8;       // 8-value chunks per row
 
   const int h = blockIdx.y;
@@ -142,71 +142,80 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
                           : static_cast<const void*>(static_cast<const uint16_t*>(p.x) + (int64_t)h * p.head_stride);
 
   // ---- 1. screen ----
+  // Keys screen one segment per pass (x needs hi and lo parts: fewer live
+  // registers); Values screen both segments together and share each A
+  // fragment between two MFMAs.
   constexpr bool kLo = KEY || F32IO;  // x needs a bf16 lo part
-  bf16x8 xh[kSegsPerWave][NG];
-  bf16x8 xl[kSegsPerWave][kLo ? NG : 1];
-  float ksq[kSegsPerWave];
-#pragma unroll
-  for (int s = 0; s < kSegsPerWave; ++s) {
-    const bool valid = l32 < seg_len[s];
-    const int64_t row = (int64_t)(seg_first[s] + (valid ? l32 : 0)) * p.token_stride;
-    ksq[s] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NG; ++ks) {
-      const int c0 = 16 * ks + 8 * half;
-      float v[8];
-      if (valid) load8<F32IO>(xin, row + c0, v);
-      else for (int i = 0; i < 8; ++i) v[i] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float xf = KEY ? s_lds[c0 + i] * v[i] : v[i];
-        ksq[s] = fmaf(xf, v[i], ksq[s]);
-        const __bf16 hb = (__bf16)xf;
-        xh[s][ks][i] = hb;
-        if constexpr (kLo) xl[s][ks][i] = (__bf16)(xf - (float)hb);
-      }
-    }
-  }
-
+  constexpr int SPP = kLo ? 1 : kSegsPerWave;  // segments per screen pass
   const uint32_t pb = 32 - __builtin_clz((uint32_t)(Cpad - 1));
   const uint32_t mask = (1u << pb) - 1u;
   float lst[kSegsPerWave][L];
 #pragma unroll
-  for (int s = 0; s < kSegsPerWave; ++s)
+  for (int pass = 0; pass < kSegsPerWave / SPP; ++pass) {
+    bf16x8 xh[SPP][NG];
+    bf16x8 xl[SPP][kLo ? NG : 1];
 #pragma unroll
-    for (int i = 0; i < L; ++i) lst[s][i] = -INFINITY;
+    for (int sp = 0; sp < SPP; ++sp) {
+      const int s = pass * SPP + sp;
+      const bool valid = l32 < seg_len[s];
+      // rows of invalid lanes are clamped to a real token and zeroed after the load
+      const int64_t row = (int64_t)(seg_first[s] + (valid ? l32 : 0)) * p.token_stride;
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        const int c0 = 16 * ks + 8 * half;
+        if constexpr (!kLo) {
+          // bf16 Values: the loaded words are the MFMA operand (x = v exactly)
+          uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) + row + c0);
+          if (!valid) w = make_uint4(0, 0, 0, 0);
+          xh[sp][ks] = __builtin_bit_cast(bf16x8, w);
+        } else {
+          float v[8];
+          load8<F32IO>(xin, row + c0, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float xf = valid ? (KEY ? s_lds[c0 + i] * v[i] : v[i]) : 0.f;
+            const __bf16 hb = (__bf16)xf;
+            xh[sp][ks][i] = hb;
+            xl[sp][ks][i] = (__bf16)(xf - (float)hb);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < L; ++i) lst[s][i] = -INFINITY;
+    }
 
-  for (int blk = 0; blk < Cpad / 32; ++blk) {
-    f32x16 acc[kSegsPerWave];
+    for (int blk = 0; blk < Cpad / 32; ++blk) {
+      f32x16 acc[SPP];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v = init[blk * 32 + 8 * (i / 4) + 4 * half + (i % 4)];
+      for (int i = 0; i < 16; ++i) {
+        const float v = init[blk * 32 + 8 * (i / 4) + 4 * half + (i % 4)];
 #pragma unroll
-      for (int s = 0; s < kSegsPerWave; ++s) acc[s][i] = v;
-    }
-    const __bf16* arow = mu_hi + (blk * 32 + l32) * ROW + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < NG; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
-#pragma unroll
-      for (int s = 0; s < kSegsPerWave; ++s) {
-        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xh[s][ks], acc[s], 0, 0, 0);
-        if constexpr (kLo) acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xl[s][ks], acc[s], 0, 0, 0);
+        for (int sp = 0; sp < SPP; ++sp) acc[sp][i] = v;
       }
-      if constexpr (F32IO) {
-        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(mu_lo + (blk * 32 + l32) * ROW + 8 * half + 16 * ks);
+      const __bf16* arow = mu_hi + (blk * 32 + l32) * ROW + 8 * half;
 #pragma unroll
-        for (int s = 0; s < kSegsPerWave; ++s)
-          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, xh[s][ks], acc[s], 0, 0, 0);
+      for (int ks = 0; ks < NG; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
+#pragma unroll
+        for (int sp = 0; sp < SPP; ++sp) {
+          acc[sp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xh[sp][ks], acc[sp], 0, 0, 0);
+          if constexpr (kLo) acc[sp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xl[sp][ks], acc[sp], 0, 0, 0);
+        }
+        if constexpr (F32IO) {
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(mu_lo + (blk * 32 + l32) * ROW + 8 * half + 16 * ks);
+#pragma unroll
+          for (int sp = 0; sp < SPP; ++sp)
+            acc[sp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, xh[sp][ks], acc[sp], 0, 0, 0);
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t c = (uint32_t)(blk * 32 + 8 * (i / 4) + 4 * half + (i % 4));
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t c = (uint32_t)(blk * 32 + 8 * (i / 4) + 4 * half + (i % 4));
 #pragma unroll
-      for (int s = 0; s < kSegsPerWave; ++s) {
-        const float key = __uint_as_float((__float_as_uint(acc[s][i]) & ~mask) | c);
-        topl_insert<L>(lst[s], key);
+        for (int sp = 0; sp < SPP; ++sp) {
+          const float key = __uint_as_float((__float_as_uint(acc[sp][i]) & ~mask) | c);
+          topl_insert<L>(lst[pass * SPP + sp], key);
+        }
       }
     }
   }
@@ -219,30 +228,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     for (int i = 0; i < L; ++i) other[i] = __shfl_xor(lst[s][i], 32);
 #pragma unroll
     for (int i = 0; i < L; ++i) topl_insert<L>(lst[s], other[i]);
-    ksq[s] += __shfl_xor(ksq[s], 32);
   }
 
   // ---- 2. certification ----
-  // |F~_c - F_c| <= eps = c1 (A + 1.01 ||x||_s maxnorm), A = maxnorm^2 / 2, with
-  // c1 = 2^-12 covering: fp32 accumulation of <= 3d+1 terms (4 (3d+2) 2^-24),
-  // the bf16 hi/lo split of x and mu (<= 2^-16), the norm's rounding (2^-24)
-  // and the key's index bits (2^(pb-23) <= 2^-14 for C <= 512).
+  // key_c is F~_c with the centre index in its low pb bits.  For every centre
+  //   |key_c - F_c| <= e_abs + r |key_c|,
+  // e_abs = (2 (n + 1) 2^-24 + 2^-17) scale bounds the fp32 accumulation of the
+  // n products and the start value in any order at up to one ulp per operation,
+  // plus the bf16 hi/lo split of x (and of mu for fp32 inputs);
+  // scale = maxnorm^2 / 2 + ||x||_s maxnorm bounds every summand's magnitude
+  // (Cauchy-Schwarz), and r = 2^(pb-23) is the truncation of the index bits.
+  // lo_bar / hi_bar below are increasing in the key, so the K_c-th and
+  // (K_c+1)-th keys decide the candidate set, and the last tracked key decides
+  // whether the tracked list holds every centre that can still be a candidate.
+  constexpr int NACC = (kLo ? 2 : 1) * D + (F32IO ? D : 0) + 1;
   const float mx = p.head_max[h * 4 + p.head_max_slot];
   const int kc = p.Kc;
   const int sidx = half;  // lane = token from here: segment `half`, token l32
   float mylst[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) mylst[i] = sidx ? lst[1][i] : lst[0][i];
-  const float myksq = sidx ? ksq[1] : ksq[0];
-  const float eps = 0x1p-12f * (0.5f * mx * mx + 1.01f * sqrtf(myksq) * mx) + 1e-30f;
-  float th = mylst[0], ph = mylst[1];
-#pragma unroll
-  for (int i = 1; i < L; ++i) {
-    if (i == kc - 1) th = mylst[i];
-    if (i == kc) ph = mylst[i];
-  }
-  const bool certain = (C <= kc) || (th - ph > 2.f * eps);
-
   const int mylen = sidx ? seg_len[1] : seg_len[0];
   const bool valid = l32 < mylen;
   const int first = sidx ? seg_first[1] : seg_first[0];
@@ -250,64 +255,45 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int frame = p.frame0 + (sidx ? seg_frame[1] : seg_frame[0]);
   const int tok_rel = first + (valid ? l32 : 0);
   const int64_t tok = p.tok0 + tok_rel;
+  const int64_t krow = (int64_t)tok_rel * p.token_stride;
+  // ||k||_s^2 of this lane's token (only used inside the error bound)
+  float myksq = 0.f;
+#pragma unroll 1
+  for (int j8 = 0; j8 < NV; ++j8) {
+    float v[8];
+    load8<F32IO>(xin, krow + 8 * j8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) myksq = fmaf(s_lds[8 * j8 + i] * v[i], v[i], myksq);
+  }
+  if (!valid) myksq = 0.f;
+  const float scale = 0.5f * mx * mx + 1.01f * sqrtf(fmaxf(myksq, 0.f)) * mx;
+  const float e_abs = (2.f * (NACC + 1) * 0x1p-24f + 0x1p-17f) * 1.001f * scale + 1e-30f;
+  const float rr = __uint_as_float((uint32_t)(127 + (int)pb - 23) << 23);
+  auto lo_bar = [&](float k) { return k - e_abs - rr * fabsf(k); };
+  auto hi_bar = [&](float k) { return k + e_abs + rr * fabsf(k); };
+  float th = mylst[0], ph = mylst[1];
+#pragma unroll
+  for (int i = 1; i < L; ++i) {
+    if (i == kc - 1) th = mylst[i];
+    if (i == kc) ph = mylst[i];
+  }
+  const bool certain = (C <= kc) || (hi_bar(ph) < lo_bar(th));
+  const bool list_covers = (C <= L) || (hi_bar(mylst[L - 1]) < lo_bar(th));
 
-  // ---- 3. lane = token: the token's row in registers ----
-  float kv[D];
-  {
-    const int64_t row = (int64_t)tok_rel * p.token_stride;
+  // ---- 3. lane = token ----
+  // The token's channels are re-read per residual group from memory (the row
+  // was just streamed in, so these reads hit the caches); the group loops stay
+  // rolled, which keeps the live state to one group at a time.
+  auto load_k16 = [&](int g, float (&k)[16]) {
+    float a[8], b[8];
+    load8<F32IO>(xin, krow + 16 * g, a);
+    load8<F32IO>(xin, krow + 16 * g + 8, b);
 #pragma unroll
-    for (int j8 = 0; j8 < NV; ++j8) {
-      float v[8];
-      load8<F32IO>(xin, row + 8 * j8, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kv[8 * j8 + i] = valid ? v[i] : 0.f;
+    for (int i = 0; i < 8; ++i) {
+      k[i] = valid ? a[i] : 0.f;
+      k[8 + i] = valid ? b[i] : 0.f;
     }
-  }
-
-  int cand[KC];
-  float tieD[KC];  // smaller is better; approximate (-key) or exact D
-#pragma unroll
-  for (int i = 0; i < KC; ++i) {
-    // clamp: only non-finite inputs can produce an index outside [0, C)
-    cand[i] = min((int)(__float_as_uint(mylst[i]) & mask), C - 1);
-    tieD[i] = -mylst[i];
-  }
-
-  if (!certain && valid) {
-    // exact fp64 rescoring of every centre: ascending (D, c)
-    double bd[KC];
-    int bc[KC];
-#pragma unroll
-    for (int i = 0; i < KC; ++i) { bd[i] = INFINITY; bc[i] = 0; }
-    for (int c = 0; c < C; ++c) {
-      double dd = 0.0;
-#pragma unroll
-      for (int j8 = 0; j8 < NV; ++j8) {
-        float m8[8];
-        if constexpr (F32IO) load8<true>(mu_g, (int64_t)c * D + 8 * j8, m8);
-        else {
-          uint4 w = *reinterpret_cast<const uint4*>(mu_hi + c * ROW + 8 * j8);
-          m8[0] = bf_lo(w.x); m8[1] = bf_hi(w.x); m8[2] = bf_lo(w.y); m8[3] = bf_hi(w.y);
-          m8[4] = bf_lo(w.z); m8[5] = bf_hi(w.z); m8[6] = bf_lo(w.w); m8[7] = bf_hi(w.w);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const double df = (double)kv[8 * j8 + i] - (double)m8[i];
-          dd = fma((double)s_lds[8 * j8 + i] * df, df, dd);
-        }
-      }
-      // sorted insertion; equal D keeps the earlier (lower) c first
-#pragma unroll
-      for (int i = KC - 1; i >= 1; --i) {
-        if (dd < bd[i - 1]) { bd[i] = bd[i - 1]; bc[i] = bc[i - 1]; }
-        else if (dd < bd[i]) { bd[i] = dd; bc[i] = c; }
-      }
-      if (dd < bd[0]) { bd[0] = dd; bc[0] = c; }
-    }
-#pragma unroll
-    for (int i = 0; i < KC; ++i) { cand[i] = bc[i]; tieD[i] = (float)bd[i]; }
-  }
-
+  };
   auto mu_row16 = [&](int c, int g, float (&m)[16]) {
     float a[8], b[8];
     if constexpr (F32IO) {
@@ -325,6 +311,69 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     for (int i = 0; i < 8; ++i) { m[i] = a[i]; m[8 + i] = b[i]; }
   };
 
+  int cand[KC];
+  float tieD[KC];  // smaller is better; approximate (-key) or exact D
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    // clamp: only non-finite inputs can produce an index outside [0, C)
+    cand[i] = min((int)(__float_as_uint(mylst[i]) & mask), C - 1);
+    tieD[i] = -mylst[i];
+  }
+
+  if (!certain && valid) {
+    // exact fp64 rescoring, ascending (D, c): of the tracked list when it holds
+    // every possible candidate, else of every centre (rare path, kept rolled)
+    auto exact_d = [&](int c) -> double {
+      double dd = 0.0;
+#pragma unroll 1
+      for (int j8 = 0; j8 < NV; ++j8) {
+        float k8[8], m8[8];
+        load8<F32IO>(xin, krow + 8 * j8, k8);
+        if constexpr (F32IO) load8<true>(mu_g, (int64_t)c * D + 8 * j8, m8);
+        else {
+          uint4 w = *reinterpret_cast<const uint4*>(mu_hi + c * ROW + 8 * j8);
+          m8[0] = bf_lo(w.x); m8[1] = bf_hi(w.x); m8[2] = bf_lo(w.y); m8[3] = bf_hi(w.y);
+          m8[4] = bf_lo(w.z); m8[5] = bf_hi(w.z); m8[6] = bf_lo(w.w); m8[7] = bf_hi(w.w);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double df = (double)k8[i] - (double)m8[i];
+          dd = fma((double)s_lds[8 * j8 + i] * df, df, dd);
+        }
+      }
+      return dd;
+    };
+    double bd[KC];
+    int bc[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) { bd[i] = INFINITY; bc[i] = 0x7fffffff; }
+    auto insert = [&](double dd, int c) {
+#pragma unroll
+      for (int i = KC - 1; i >= 0; --i) {
+        const bool before_prev = i > 0 && (dd < bd[i > 0 ? i - 1 : 0] ||
+                                           (dd == bd[i > 0 ? i - 1 : 0] && c < bc[i > 0 ? i - 1 : 0]));
+        const bool before_this = dd < bd[i] || (dd == bd[i] && c < bc[i]);
+        if (before_prev) { bd[i] = bd[i - 1]; bc[i] = bc[i - 1]; }
+        else if (before_this) { bd[i] = dd; bc[i] = c; }
+      }
+    };
+    if (list_covers) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        const int c = (int)(__float_as_uint(mylst[i]) & mask);
+        if (c < C) insert(exact_d(c), c);
+      }
+    } else {
+#pragma unroll 1
+      for (int c = 0; c < C; ++c) insert(exact_d(c), c);
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      cand[i] = min(bc[i], C - 1);
+      tieD[i] = (float)bd[i];
+    }
+  }
+
   // ---- QSAC stage 2: expected INT2 logit perturbation of each candidate ----
   int chosen = cand[0];
   if constexpr (KEY && KC > 1) {
@@ -333,30 +382,30 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       double bestP = INFINITY;
       float bestD = INFINITY;
       int best = 0x7fffffff;
-      for (int i = 0; i < kc; ++i) {
-        int c = cand[0];
-        float td = tieD[0];
 #pragma unroll
-        for (int q = 1; q < KC; ++q)
-          if (q == i) { c = cand[q]; td = tieD[q]; }
-        if (c >= C) continue;  // padding rows when C < K_c
-        double P = 0.0;
+      for (int i = 0; i < KC; ++i) {
+        const int c = cand[i];
+        if (i < kc && c < C) {  // c >= C: padding rows when C < K_c
+          double P = 0.0;
+#pragma unroll 1
+          for (int g = 0; g < NG; ++g) {
+            float k[16], m[16];
+            load_k16(g, k);
+            mu_row16(c, g, m);
+            float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          float m[16];
-          mu_row16(c, g, m);
-          float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float rho = kv[16 * g + j] - m[j];
-            lo = fminf(lo, rho);
-            hi = fmaxf(hi, rho);
+            for (int j = 0; j < 16; ++j) {
+              const float rho = k[j] - m[j];
+              lo = fminf(lo, rho);
+              hi = fmaxf(hi, rho);
+            }
+            const double rg = (double)hi - (double)lo;
+            P = fma(p.uniform ? 16.0 : sg[g], rg * rg, P);
           }
-          const double rg = (double)hi - (double)lo;
-          P = fma(p.uniform ? 16.0 : sg[g], rg * rg, P);
+          const float td = tieD[i];
+          const bool better = (P < bestP) || (P == bestP && (td < bestD || (td == bestD && c < best)));
+          if (better) { bestP = P; bestD = td; best = c; }
         }
-        const bool better = (P < bestP) || (P == bestP && (td < bestD || (td == bestD && c < best)));
-        if (better) { bestP = P; bestD = td; best = c; }
       }
       chosen = best < C ? best : cand[0];  // all-NaN scores keep a valid index
     }
@@ -365,21 +414,22 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   // ---- INT2 residual tiles and PSAC ----
   const int T = p.T;
   const int tile = frame * p.tpf + pos / T;
-  uint32_t words[NG];
+  const int64_t slot = (int64_t)h * p.Ncap + tok;
   double cacc[R > 0 ? R : 1];
 #pragma unroll
   for (int i = 0; i < (R > 0 ? R : 1); ++i) cacc[i] = 0.0;
   const double* U = p.u64 + (int64_t)h * D * p.rp;
 
-#pragma unroll
+#pragma unroll 1
   for (int g = 0; g < NG; ++g) {
-    float m[16];
+    float k[16], m[16];
+    load_k16(g, k);
     mu_row16(chosen, g, m);
     float rho[16];
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      rho[j] = kv[16 * g + j] - m[j];
+      rho[j] = k[j] - m[j];
       lo = fminf(lo, rho[j]);
       hi = fmaxf(hi, rho[j]);
     }
@@ -401,24 +451,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       w |= code << (2 * j);
       if constexpr (KEY && R > 0) {
         const float rhat = fmaf((float)code, sf, zf);
-        const double e = ((double)kv[16 * g + j] - (double)m[j]) - (double)rhat;
+        const double e = ((double)k[j] - (double)m[j]) - (double)rhat;
         const double* urow = U + (int64_t)(16 * g + j) * p.rp;
 #pragma unroll
         for (int i = 0; i < R; ++i) cacc[i] = fma(urow[i], e, cacc[i]);
       }
     }
-    words[g] = w;
-    if (valid && (pos % T) == 0)
-      p.params[((int64_t)h * p.Pcap + tile) * NG + g] = (uint32_t)zb | ((uint32_t)sb << 16);
+    if (valid) {
+      p.codes[slot * NG + g] = w;
+      if ((pos % T) == 0) p.params[((int64_t)h * p.Pcap + tile) * NG + g] = (uint32_t)zb | ((uint32_t)sb << 16);
+    }
   }
 
   if (!valid) return;
-  const int64_t slot = (int64_t)h * p.Ncap + tok;
   if (p.idx_bytes == 1) static_cast<uint8_t*>(p.idx)[slot] = (uint8_t)chosen;
   else static_cast<uint16_t*>(p.idx)[slot] = (uint16_t)chosen;
-  uint4* cw = reinterpret_cast<uint4*>(p.codes + slot * NG);
-#pragma unroll
-  for (int q = 0; q < NG / 4; ++q) cw[q] = make_uint4(words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
 
   if constexpr (KEY && R > 0) {
     const int r = p.r;
