@@ -10,7 +10,10 @@ hipError_t launch_append_d128_f32(const AppendParams& p, int heads, bool key, hi
 
 size_t append_lds_bytes(int Cpad, int head_dim, bool f32io) {
   const size_t row = (size_t)(head_dim + 8) * 2;
-  return (size_t)Cpad * row * (f32io ? 2 : 1) + (size_t)Cpad * 4 + (size_t)head_dim * 4;
+  // codebook (bf16 rows; fp32 activations add a lo copy), start values, s, and
+  // the fp64 U of PSAC (at most 16 columns)
+  return (size_t)Cpad * row * (f32io ? 2 : 1) + (size_t)Cpad * 4 + (size_t)head_dim * 4 +
+         (size_t)head_dim * 16 * 8;
 }
 
 hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io, bool key,

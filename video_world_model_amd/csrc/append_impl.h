@@ -46,6 +46,11 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return __half2float(__ushort_as_half(b));
 }
 
+// min / max through v_med3 (no NaN canonicalisation; inputs are finite or
+// +-inf by construction)
+__device__ __forceinline__ float fmin_fast(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -INFINITY); }
+__device__ __forceinline__ float fmax_fast(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
 // Insert a key into a descending list of L keys (keeps the L largest).
 template <int L>
 __device__ __forceinline__ void topl_insert(float (&l)[L], float x) {
@@ -90,6 +95,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   __bf16* mu_lo = mu_hi + Cpad * ROW;  // used for fp32 activations only
   float* init = reinterpret_cast<float*>(mu_hi + Cpad * ROW * (F32IO ? 2 : 1));
   float* s_lds = init + Cpad;
+  double* u_lds = reinterpret_cast<double*>(s_lds + D);  // [D][rp] fp64 (Keys with PSAC only)
 
   const void* mu_g = F32IO ? static_cast<const void*>(static_cast<const float*>(p.mu) + (int64_t)h * C * D)
                            : static_cast<const void*>(static_cast<const uint16_t*>(p.mu) + (int64_t)h * C * D);
@@ -118,6 +124,8 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
     init[c] = c < C ? -p.norm_half[(int64_t)h * C + c] : -3.0e38f;
   for (int j = threadIdx.x; j < D; j += 256)
     s_lds[j] = p.uniform ? 1.f : p.sens[(int64_t)h * D + j];
+  if constexpr (KEY && R > 0)
+    for (int e = threadIdx.x; e < D * p.rp; e += 256) u_lds[e] = p.u64[(int64_t)h * D * p.rp + e];
   __syncthreads();
 
   // ---- segments of this wave ----
@@ -256,16 +264,40 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   const int tok_rel = first + (valid ? l32 : 0);
   const int64_t tok = p.tok0 + tok_rel;
   const int64_t krow = (int64_t)tok_rel * p.token_stride;
+  // the token's row, loaded once into registers (packed bf16 pairs, or fp32);
+  // invalid lanes hold a clamped real row and are masked at every reduction
+  // and store
+  uint32_t kw[F32IO ? D : D / 2];
+#pragma unroll
+  for (int j8 = 0; j8 < NV; ++j8) {
+    if constexpr (F32IO) {
+      float v[8];
+      load8<true>(xin, krow + 8 * j8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kw[8 * j8 + i] = __float_as_uint(v[i]);
+    } else {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) + krow + 8 * j8);
+      kw[4 * j8 + 0] = w.x;
+      kw[4 * j8 + 1] = w.y;
+      kw[4 * j8 + 2] = w.z;
+      kw[4 * j8 + 3] = w.w;
+    }
+  }
+  // Register fence on the packed row: an empty asm that the compiler must
+  // assume rewrites the words, so unpacked copies are not kept alive across
+  // phases (it emits no instruction).
+  auto fence_row = [&]() {
+#pragma unroll
+    for (int i = 0; i < (F32IO ? D : D / 2); ++i) asm volatile("" : "+v"(kw[i]));
+  };
+  auto kval = [&](int j) -> float {
+    if constexpr (F32IO) return __uint_as_float(kw[j]);
+    else return (j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1]);
+  };
   // ||k||_s^2 of this lane's token (only used inside the error bound)
   float myksq = 0.f;
-#pragma unroll 1
-  for (int j8 = 0; j8 < NV; ++j8) {
-    float v[8];
-    load8<F32IO>(xin, krow + 8 * j8, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) myksq = fmaf(s_lds[8 * j8 + i] * v[i], v[i], myksq);
-  }
-  if (!valid) myksq = 0.f;
+  for (int j = 0; j < D; ++j) myksq = fmaf(s_lds[j] * kval(j), kval(j), myksq);
   const float scale = 0.5f * mx * mx + 1.01f * sqrtf(fmaxf(myksq, 0.f)) * mx;
   const float e_abs = (2.f * (NACC + 1) * 0x1p-24f + 0x1p-17f) * 1.001f * scale + 1e-30f;
   const float rr = __uint_as_float((uint32_t)(127 + (int)pb - 23) << 23);
@@ -284,14 +316,28 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   // The token's channels are re-read per residual group from memory (the row
   // was just streamed in, so these reads hit the caches); the group loops stay
   // rolled, which keeps the live state to one group at a time.
+  // The 16 channels of residual group g (g is wave-uniform): a switch on g
+  // becomes scalar branches, so the row stays in registers with static indices.
   auto load_k16 = [&](int g, float (&k)[16]) {
-    float a[8], b[8];
-    load8<F32IO>(xin, krow + 16 * g, a);
-    load8<F32IO>(xin, krow + 16 * g + 8, b);
+    constexpr int WPG = F32IO ? 16 : 8;  // row words per group
+    uint32_t w[WPG];
+    switch (g) {
+#define QWM_GROUP_CASE(G)                                              \
+      case G:                                                          \
+        if constexpr (G < NG) {                                        \
+          _Pragma("unroll") for (int i = 0; i < WPG; ++i) w[i] = kw[G * WPG + i]; \
+        }                                                              \
+        break;
+      QWM_GROUP_CASE(0) QWM_GROUP_CASE(1) QWM_GROUP_CASE(2) QWM_GROUP_CASE(3)
+      QWM_GROUP_CASE(4) QWM_GROUP_CASE(5) QWM_GROUP_CASE(6) QWM_GROUP_CASE(7)
+#undef QWM_GROUP_CASE
+      default:
+        break;
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      k[i] = valid ? a[i] : 0.f;
-      k[8 + i] = valid ? b[i] : 0.f;
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (F32IO) k[i] = __uint_as_float(w[i]);
+      else k[i] = (i & 1) ? bf_hi(w[i >> 1]) : bf_lo(w[i >> 1]);
     }
   };
   auto mu_row16 = [&](int c, int g, float (&m)[16]) {
@@ -322,23 +368,19 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
 
   if (!certain && valid) {
     // exact fp64 rescoring, ascending (D, c): of the tracked list when it holds
-    // every possible candidate, else of every centre (rare path, kept rolled)
+    // every possible candidate, else of every centre (rare); D_c from the
+    // register row, one residual group at a time
     auto exact_d = [&](int c) -> double {
       double dd = 0.0;
 #pragma unroll 1
-      for (int j8 = 0; j8 < NV; ++j8) {
-        float k8[8], m8[8];
-        load8<F32IO>(xin, krow + 8 * j8, k8);
-        if constexpr (F32IO) load8<true>(mu_g, (int64_t)c * D + 8 * j8, m8);
-        else {
-          uint4 w = *reinterpret_cast<const uint4*>(mu_hi + c * ROW + 8 * j8);
-          m8[0] = bf_lo(w.x); m8[1] = bf_hi(w.x); m8[2] = bf_lo(w.y); m8[3] = bf_hi(w.y);
-          m8[4] = bf_lo(w.z); m8[5] = bf_hi(w.z); m8[6] = bf_lo(w.w); m8[7] = bf_hi(w.w);
-        }
+      for (int g = 0; g < NG; ++g) {
+        float k[16], m[16];
+        load_k16(g, k);
+        mu_row16(c, g, m);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const double df = (double)k8[i] - (double)m8[i];
-          dd = fma((double)s_lds[8 * j8 + i] * df, df, dd);
+        for (int i = 0; i < 16; ++i) {
+          const double df = (double)k[i] - (double)m[i];
+          dd = fma((double)s_lds[16 * g + i] * df, df, dd);
         }
       }
       return dd;
@@ -358,9 +400,13 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
       }
     };
     if (list_covers) {
-#pragma unroll
+#pragma unroll 1
       for (int i = 0; i < L; ++i) {
-        const int c = (int)(__float_as_uint(mylst[i]) & mask);
+        float key = mylst[0];
+#pragma unroll
+        for (int q = 1; q < L; ++q)
+          if (q == i) key = mylst[q];
+        const int c = (int)(__float_as_uint(key) & mask);
         if (c < C) insert(exact_d(c), c);
       }
     } else {
@@ -375,6 +421,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   }
 
   // ---- QSAC stage 2: expected INT2 logit perturbation of each candidate ----
+  fence_row();
   int chosen = cand[0];
   if constexpr (KEY && KC > 1) {
     if (p.use_range) {
@@ -382,10 +429,14 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
       double bestP = INFINITY;
       float bestD = INFINITY;
       int best = 0x7fffffff;
+#pragma unroll 1
+      for (int i = 0; i < kc; ++i) {
+        int c = cand[0];
+        float td = tieD[0];
 #pragma unroll
-      for (int i = 0; i < KC; ++i) {
-        const int c = cand[i];
-        if (i < kc && c < C) {  // c >= C: padding rows when C < K_c
+        for (int q = 1; q < KC; ++q)
+          if (q == i) { c = cand[q]; td = tieD[q]; }
+        if (c < C) {  // c >= C: padding rows when C < K_c
           double P = 0.0;
 #pragma unroll 1
           for (int g = 0; g < NG; ++g) {
@@ -396,13 +447,12 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
               const float rho = k[j] - m[j];
-              lo = fminf(lo, rho);
-              hi = fmaxf(hi, rho);
+              lo = fmin_fast(lo, rho);
+              hi = fmax_fast(hi, rho);
             }
             const double rg = (double)hi - (double)lo;
             P = fma(p.uniform ? 16.0 : sg[g], rg * rg, P);
           }
-          const float td = tieD[i];
           const bool better = (P < bestP) || (P == bestP && (td < bestD || (td == bestD && c < best)));
           if (better) { bestP = P; bestD = td; best = c; }
         }
@@ -412,13 +462,14 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   }
 
   // ---- INT2 residual tiles and PSAC ----
+  fence_row();
   const int T = p.T;
   const int tile = frame * p.tpf + pos / T;
   const int64_t slot = (int64_t)h * p.Ncap + tok;
   double cacc[R > 0 ? R : 1];
 #pragma unroll
   for (int i = 0; i < (R > 0 ? R : 1); ++i) cacc[i] = 0.0;
-  const double* U = p.u64 + (int64_t)h * D * p.rp;
+  const double* U = u_lds;
 
 #pragma unroll 1
   for (int g = 0; g < NG; ++g) {
@@ -430,13 +481,13 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       rho[j] = k[j] - m[j];
-      lo = fminf(lo, rho[j]);
-      hi = fmaxf(hi, rho[j]);
+      lo = fmin_fast(lo, rho[j]);
+      hi = fmax_fast(hi, rho[j]);
     }
     if (!valid) { lo = INFINITY; hi = -INFINITY; }
     for (int off = 1; off < T; off <<= 1) {
-      lo = fminf(lo, __shfl_xor(lo, off));
-      hi = fmaxf(hi, __shfl_xor(hi, off));
+      lo = fmin_fast(lo, __shfl_xor(lo, off));
+      hi = fmax_fast(hi, __shfl_xor(hi, off));
     }
     const uint16_t zb = to_half_bits(lo);
     const uint16_t sb = to_half_bits((hi - lo) / 3.0f);
@@ -446,8 +497,8 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      uint32_t code = 0;
-      if (sf != 0.f) code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
+      uint32_t code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
+      code = sf != 0.f ? code : 0u;  // a zero scale codes everything as 0
       w |= code << (2 * j);
       if constexpr (KEY && R > 0) {
         const float rhat = fmaf((float)code, sf, zf);
@@ -455,6 +506,12 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
         const double* urow = U + (int64_t)(16 * g + j) * p.rp;
 #pragma unroll
         for (int i = 0; i < R; ++i) cacc[i] = fma(urow[i], e, cacc[i]);
+        // one U row in flight at a time: the empty asm statements below (they
+        // emit no instruction) pin this row's FMAs before the next row's LDS
+        // reads, so the rows are not all loaded up front
+#pragma unroll
+        for (int i = 0; i < R; ++i) asm volatile("" : "+v"(cacc[i]));
+        asm volatile("" ::: "memory");
       }
     }
     if (valid) {
@@ -507,7 +564,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
 
 template <int D, bool F32IO, bool KEY, int KC, int R>
 hipError_t launch_one(const AppendParams& p, int heads, hipStream_t stream) {
-  const size_t lds = append_lds_bytes(p.Cpad, D, F32IO);
+  const size_t lds = append_lds_bytes(p.Cpad, D, F32IO);  // includes room for U
   auto fn = append_kernel<D, F32IO, KEY, KC, R>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

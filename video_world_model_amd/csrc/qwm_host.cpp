@@ -421,10 +421,14 @@ QWM_API int qwm_calib_import(const qwm_config* cfg, void* calib, const float* mu
     hm[h * 4 + 2] = (float)(mv * (1 + 1e-6));
     hm[h * 4 + 3] = 0.f;
   }
+  // Blocking copy after draining the caller's stream: the block is complete
+  // in device memory when this call returns.
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(calib, blk.data(), blk.size(), hipMemcpyHostToDevice, s);
+  hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
-  e = hipStreamSynchronize(s);
+  e = hipMemcpy(calib, blk.data(), blk.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e);
   return QWM_OK;
 }
@@ -441,22 +445,37 @@ QWM_API int qwm_calibrate(const qwm_config* cfg, void* calib, const void* q_hist
   if (n_kv < std::max(cfg->num_centroids_k, cfg->num_centroids_v) || iters < 0) return QWM_ERR_INVALID_ARG;
   const int H = cfg->num_heads, d = cfg->head_dim, es = esize(cfg);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto fetch = [&](const void* src, int64_t n, const qwm_strides* sd, std::vector<float>& dst) -> int {
-    std::vector<unsigned char> raw((size_t)H * n * d * es);
-    for (int h = 0; h < H; ++h) {
-      hipError_t e = hipMemcpy2DAsync(&raw[(size_t)h * n * d * es], (size_t)d * es,
-                                      static_cast<const unsigned char*>(src) + (size_t)h * sd->head * es,
-                                      (size_t)sd->token * es, (size_t)d * es, (size_t)n, hipMemcpyDeviceToHost, s);
-      if (e != hipSuccess) return hip_fail(e);
-    }
+  // the inputs are produced on the caller's stream: drain it, then copy with
+  // blocking copies (complete on return)
+  {
     hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e);
+  }
+  // Device -> host through a pinned staging buffer (blocking 2D copies, one per
+  // head), then widened to fp32.
+  auto fetch = [&](const void* src, int64_t n, const qwm_strides* sd, std::vector<float>& dst) -> int {
+    const size_t bytes = (size_t)H * n * d * es;
+    void* stage = nullptr;
+    hipError_t e = hipHostMalloc(&stage, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e);
+    unsigned char* raw = static_cast<unsigned char*>(stage);
+    for (int h = 0; h < H && e == hipSuccess; ++h)
+      e = hipMemcpy2D(raw + (size_t)h * n * d * es, (size_t)d * es,
+                      static_cast<const unsigned char*>(src) + (size_t)h * sd->head * es, (size_t)sd->token * es,
+                      (size_t)d * es, (size_t)n, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      hipHostFree(stage);
+      return hip_fail(e);
+    }
     dst.resize((size_t)H * n * d);
-    if (es == 4) std::memcpy(dst.data(), raw.data(), raw.size());
+    if (es == 4) std::memcpy(dst.data(), raw, bytes);
     else {
-      const uint16_t* b = reinterpret_cast<const uint16_t*>(raw.data());
+      const uint16_t* b = reinterpret_cast<const uint16_t*>(raw);
       for (size_t i = 0; i < dst.size(); ++i) dst[i] = bf16_bits_to_f32(b[i]);
     }
+    e = hipHostFree(stage);
+    if (e != hipSuccess) return hip_fail(e);
     return QWM_OK;
   };
   std::vector<float> q, k, v;
