@@ -13,7 +13,7 @@ size_t append_lds_bytes(int Cpad, int head_dim, bool f32io) {
   // codebook (bf16 rows; fp32 activations add a lo copy), start values, s, and
   // the fp64 U of PSAC (at most 16 columns)
   return (size_t)Cpad * row * (f32io ? 2 : 1) + (size_t)Cpad * 4 + (size_t)head_dim * 4 +
-         (size_t)head_dim * 16 * 8;
+         (size_t)head_dim * 8 + (size_t)head_dim * 16 * 8 + (size_t)4 * head_dim * 4;
 }
 
 hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io, bool key,

@@ -95,7 +95,10 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   __bf16* mu_lo = mu_hi + Cpad * ROW;  // used for fp32 activations only
   float* init = reinterpret_cast<float*>(mu_hi + Cpad * ROW * (F32IO ? 2 : 1));
   float* s_lds = init + Cpad;
-  double* u_lds = reinterpret_cast<double*>(s_lds + D);  // [D][rp] fp64 (Keys with PSAC only)
+  double* s64_lds = reinterpret_cast<double*>(s_lds + D);  // [D] fp64 copy of s
+  double* u_lds = s64_lds + D;                              // [D][rp] fp64 (Keys with PSAC only)
+  // per-wave row buffer for the rare all-centre search (D words per wave)
+  uint32_t* row_lds = reinterpret_cast<uint32_t*>(u_lds + D * 16) + wave * D;
 
   const void* mu_g = F32IO ? static_cast<const void*>(static_cast<const float*>(p.mu) + (int64_t)h * C * D)
                            : static_cast<const void*>(static_cast<const uint16_t*>(p.mu) + (int64_t)h * C * D);
@@ -122,8 +125,11 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   }
   for (int c = threadIdx.x; c < Cpad; c += 256)
     init[c] = c < C ? -p.norm_half[(int64_t)h * C + c] : -3.0e38f;
-  for (int j = threadIdx.x; j < D; j += 256)
-    s_lds[j] = p.uniform ? 1.f : p.sens[(int64_t)h * D + j];
+  for (int j = threadIdx.x; j < D; j += 256) {
+    const float sj = p.uniform ? 1.f : p.sens[(int64_t)h * D + j];
+    s_lds[j] = sj;
+    s64_lds[j] = (double)sj;
+  }
   if constexpr (KEY && R > 0)
     for (int e = threadIdx.x; e < D * p.rp; e += 256) u_lds[e] = p.u64[(int64_t)h * D * p.rp + e];
   __syncthreads();
@@ -358,7 +364,9 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   };
 
   int cand[KC];
-  float tieD[KC];  // smaller is better; approximate (-key) or exact D
+  // tie-break value for QSAC stage 2 (smaller is better), on the -F scale:
+  // -key, or (D - ||k||_s^2) / 2 for centres that were rescored exactly
+  float tieD[KC];
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     // clamp: only non-finite inputs can produce an index outside [0, C)
@@ -366,58 +374,137 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
     tieD[i] = -mylst[i];
   }
 
-  if (!certain && valid) {
-    // exact fp64 rescoring, ascending (D, c): of the tracked list when it holds
-    // every possible candidate, else of every centre (rare); D_c from the
-    // register row, one residual group at a time
-    auto exact_d = [&](int c) -> double {
-      double dd = 0.0;
+  // D_c = sum_j s_j (k_j - mu_cj)^2 in fp64 for one centre, the row given by
+  // `row_word` (register row, or a broadcast one).  For bf16 inputs k - mu is
+  // exact in fp32; the products and the sum are fp64.
+  auto exact_d_row = [&](int c, auto&& row_words) -> double {
+    double dd = 0.0;
 #pragma unroll 1
-      for (int g = 0; g < NG; ++g) {
-        float k[16], m[16];
-        load_k16(g, k);
-        mu_row16(c, g, m);
+    for (int g = 0; g < NG; ++g) {
+      float k[16], m[16];
+      row_words(g, k);
+      mu_row16(c, g, m);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const double df = (double)k[i] - (double)m[i];
-          dd = fma((double)s_lds[16 * g + i] * df, df, dd);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const double df = F32IO ? (double)k[i] - (double)m[i] : (double)(k[i] - m[i]);
+        dd = fma(s64_lds[16 * g + i] * df, df, dd);
       }
-      return dd;
-    };
-    double bd[KC];
-    int bc[KC];
+    }
+    return dd;
+  };
+  // exact top-K_c buffer, ascending (D, c)
+  double bd[KC];
+  int bc[KC];
+  auto reset_best = [&]() {
 #pragma unroll
     for (int i = 0; i < KC; ++i) { bd[i] = INFINITY; bc[i] = 0x7fffffff; }
-    auto insert = [&](double dd, int c) {
+  };
+  auto insert = [&](double dd, int c) {
 #pragma unroll
-      for (int i = KC - 1; i >= 0; --i) {
-        const bool before_prev = i > 0 && (dd < bd[i > 0 ? i - 1 : 0] ||
-                                           (dd == bd[i > 0 ? i - 1 : 0] && c < bc[i > 0 ? i - 1 : 0]));
-        const bool before_this = dd < bd[i] || (dd == bd[i] && c < bc[i]);
-        if (before_prev) { bd[i] = bd[i - 1]; bc[i] = bc[i - 1]; }
-        else if (before_this) { bd[i] = dd; bc[i] = c; }
-      }
-    };
-    if (list_covers) {
+    for (int i = KC - 1; i >= 0; --i) {
+      const int ip = i > 0 ? i - 1 : 0;
+      const bool before_prev = i > 0 && (dd < bd[ip] || (dd == bd[ip] && c < bc[ip]));
+      const bool before_this = dd < bd[i] || (dd == bd[i] && c < bc[i]);
+      if (before_prev) { bd[i] = bd[i - 1]; bc[i] = bc[i - 1]; }
+      else if (before_this) { bd[i] = dd; bc[i] = c; }
+    }
+  };
+
+  // (1) Band rescoring.  Tracked entries whose lower bar clears the upper bar
+  // of the (K_c+1)-th key are surely candidates (a prefix [0, m)); entries whose
+  // upper bar is below the K_c-th key's lower bar are surely not (from index a
+  // on).  Only [m, a) is rescored exactly, for the remaining K_c - m slots.
+  const bool need_band = !certain && list_covers && valid;
+  int m_sure = 0, a_end = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (i < kc && lo_bar(mylst[i]) > hi_bar(ph)) m_sure = i + 1;
+    if (hi_bar(mylst[i]) >= lo_bar(th)) a_end = i + 1;
+  }
+  if (__any(need_band)) {
+    reset_best();
 #pragma unroll 1
-      for (int i = 0; i < L; ++i) {
+    for (int i = 0; i < L; ++i) {
+      const bool mine = need_band && i >= m_sure && i < a_end;
+      if (!__any(mine)) continue;
+      if (mine) {
         float key = mylst[0];
 #pragma unroll
         for (int q = 1; q < L; ++q)
           if (q == i) key = mylst[q];
         const int c = (int)(__float_as_uint(key) & mask);
-        if (c < C) insert(exact_d(c), c);
+        if (c < C) insert(exact_d_row(c, load_k16), c);
       }
-    } else {
-#pragma unroll 1
-      for (int c = 0; c < C; ++c) insert(exact_d(c), c);
     }
+    if (need_band) {
+      // slots [m_sure, kc) take the exact winners in order
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      cand[i] = min(bc[i], C - 1);
-      tieD[i] = (float)bd[i];
+      for (int q = 0; q < KC; ++q) {
+        const int src = q - m_sure;  // rank among the rescored entries
+        if (q >= m_sure && q < kc) {
+          int c = bc[0];
+          double dd = bd[0];
+#pragma unroll
+          for (int r = 1; r < KC; ++r)
+            if (r == src) { c = bc[r]; dd = bd[r]; }
+          cand[q] = min(c, C - 1);
+          tieD[q] = (float)(0.5 * (dd - (double)myksq));
+        }
+      }
     }
+  }
+
+  // (2) Rare: the tracked list does not hold every possible candidate.  The
+  // whole wave searches all centres for one such token at a time: its row is
+  // broadcast to scalar registers and lane l scores centres l, l+64, ...
+  uint64_t full = __ballot(!certain && !list_covers && valid);
+  while (full) {
+    const int t = __builtin_ctzll(full);
+    full &= full - 1;
+    constexpr int KWN = F32IO ? D : D / 2;
+    if (lane == t) {
+#pragma unroll
+      for (int i = 0; i < KWN; i += 4)
+        *reinterpret_cast<uint4*>(row_lds + i) = make_uint4(kw[i], kw[i + 1], kw[i + 2], kw[i + 3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the row is in LDS for every lane
+    auto bcast_k16 = [&](int g, float (&k)[16]) {
+      constexpr int WPG = F32IO ? 16 : 8;
+      const uint32_t* src = row_lds + g * WPG;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (F32IO) k[i] = __uint_as_float(src[i]);
+        else k[i] = (i & 1) ? bf_hi(src[i >> 1]) : bf_lo(src[i >> 1]);
+      }
+    };
+    reset_best();
+#pragma unroll 1
+    for (int c = lane; c < C; c += 64) insert(exact_d_row(c, bcast_k16), c);
+    // K_c rounds of a wave-wide lexicographic (D, c) minimum
+    const float ksq_t = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(myksq), t));
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+      double wd = bd[0];
+      int wc = bc[0];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double od = __shfl_xor(wd, off);
+        const int oc = __shfl_xor(wc, off);
+        if (od < wd || (od == wd && oc < wc)) { wd = od; wc = oc; }
+      }
+      if (bc[0] == wc) {  // the owner pops its head
+#pragma unroll
+        for (int r = 0; r < KC - 1; ++r) { bd[r] = bd[r + 1]; bc[r] = bc[r + 1]; }
+        bd[KC - 1] = INFINITY;
+        bc[KC - 1] = 0x7fffffff;
+      }
+      if (lane == t && q < kc) {
+        cand[q] = min(wc, C - 1);
+        tieD[q] = (float)(0.5 * (wd - (double)ksq_t));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // all reads of this row precede the next write
   }
 
   // ---- QSAC stage 2: expected INT2 logit perturbation of each candidate ----
