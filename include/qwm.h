@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define QWM_ABI_VERSION 1
+#define QWM_ABI_VERSION 2
 
 /* status codes */
 #define QWM_OK 0
@@ -106,6 +106,11 @@ typedef struct qwm_strides {
  *   norm_k  [H][C_K]    fp32 ||mu||^2 / 2
  *   norm_v  [H][C_V]    fp32 ||mu||^2 / 2
  *   head_max [H][4]     fp32 max_c ||mu_K||_s, max_c ||mu_K||, max_c ||mu_V||, 0
+ *   mu_k16 [H][C_K][d]  fp16 copy of mu_k for the bf16 attention path; inside
+ *                       each 16-channel group, position 2j holds channel j and
+ *                       position 2j+1 channel j+8 (j = 0..7)
+ *   mu_v16 [H][C_V][d]  the same for mu_v
+ *   ut16   [H][16][d]   fp16 U^T in the same channel order; rows >= r are zero
  *
  * Cache block (capacity N = max_frames*F tokens, P = max_frames*ceil(F/T)
  * parameter tiles per head):
@@ -124,7 +129,7 @@ typedef struct qwm_layout_info {
   uint64_t cache_bytes;
   uint64_t token_capacity;
   uint64_t tile_capacity;
-  uint64_t mu_k, mu_v, sens, u, u64, sgroup, norm_kw, norm_k, norm_v, head_max;
+  uint64_t mu_k, mu_v, sens, u, u64, sgroup, norm_kw, norm_k, norm_v, head_max, mu_k16, mu_v16, ut16;
   uint64_t idx_k, codes_k, params_k, coef, coef_scale, idx_v, codes_v, params_v;
   uint32_t idx_k_bytes, idx_v_bytes;
 } qwm_layout_info;

@@ -62,7 +62,7 @@ def test_layout_alignment_and_sizes():
     for name, w in workloads.WORKLOADS.items():
         L = qwm.layout(cfg_of(w))
         for f in ["mu_k", "mu_v", "sens", "u", "u64", "sgroup", "norm_kw", "norm_k", "norm_v", "head_max",
-                  "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]:
+                  "mu_k16", "mu_v16", "ut16", "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]:
             assert L[f] % 256 == 0
         assert L["token_capacity"] == w.n_tokens
         assert L["tile_capacity"] == w.frames * -(-w.frame_tokens // w.group_tokens)

@@ -176,7 +176,11 @@ def test_split_kv_matches_single_and_empty_cache():
     ref = o_one.float().cpu().numpy()
     diff = np.abs(o_split.float().cpu().numpy() - ref)
     assert np.all(diff <= 4 * P.bf16_half_ulp(ref) + 1e-3)
-    assert float((l_split - l_one).abs().max()) <= 1e-4
+    # the sum of probabilities is taken over the fp16-rounded values that enter
+    # P V, each within 2^-11 relative of the exact one, and every split rounds
+    # at its own running max: each lse is within log(1 + 2^-11) of the exact
+    # one, so the two differ by at most about 2^-10
+    assert float((l_split - l_one).abs().max()) <= 2.0 ** -10
     # empty cache: zero output, lse = -inf
     empty = qwm.Cache(cfg, cache.calib)
     o0, l0 = qwm.attention(empty, q)

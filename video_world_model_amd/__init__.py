@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqwm.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGN, ERR_CAPACITY, ERR_STATE, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE = 1, 2, 3
@@ -40,7 +40,7 @@ class QwmStrides(ctypes.Structure):
 
 _LAYOUT_FIELDS = ["calib_bytes", "cache_bytes", "token_capacity", "tile_capacity",
                   "mu_k", "mu_v", "sens", "u", "u64", "sgroup", "norm_kw", "norm_k", "norm_v", "head_max",
-                  "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]
+                  "mu_k16", "mu_v16", "ut16", "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]
 
 
 class QwmLayout(ctypes.Structure):

@@ -396,8 +396,7 @@ hipError_t launch_d(const AttnParams& p, int heads, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1 || p.top1 || p.logits) return e;
-  hipLaunchKernelGGL((combine_kernel<D, F32IO>), dim3(p.n_q, heads), dim3(D), 0, stream, p, heads);
-  return hipGetLastError();
+  return launch_combine(p, heads, D, F32IO, stream);
 }
 
 // Top-1 over original keys: one thread per (head, query), fp32 dot products.
@@ -438,7 +437,22 @@ __global__ __launch_bounds__(256) void dense_top1_kernel(const void* q, int64_t 
 
 }  // namespace
 
+hipError_t launch_combine(const AttnParams& p, int heads, int head_dim, bool f32io, hipStream_t stream) {
+  const dim3 grid(p.n_q, heads);
+  if (head_dim == 128) {
+    if (f32io) hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(128), 0, stream, p, heads);
+    else hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(128), 0, stream, p, heads);
+  } else {
+    if (f32io) hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(64), 0, stream, p, heads);
+    else hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(64), 0, stream, p, heads);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnParams& p, int heads, int head_dim, bool f32io, hipStream_t stream) {
+  // bf16 softmax attention has its own kernel; fp32 activations and the
+  // logits / top-1 exports use the generic one
+  if (!f32io && !p.logits && !p.top1) return launch_attention_bf16(p, heads, head_dim, stream);
   if (head_dim == 128) return f32io ? launch_d<128, true>(p, heads, stream) : launch_d<128, false>(p, heads, stream);
   return f32io ? launch_d<64, true>(p, heads, stream) : launch_d<64, false>(p, heads, stream);
 }

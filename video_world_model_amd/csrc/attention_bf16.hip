@@ -1,0 +1,409 @@
+// Attention over the compressed cache, bf16 activations, for gfx950 (CDNA4).
+//
+// Method: QuantWM rebuilds each Key as centre + dequantized 2-bit residual +
+// U c_hat, the PSAC compensation applied at cache reconstruction ([digest]
+// "Flickering after quantization? ...", PSAC paragraph; [review] summary: a
+// low-rank correction of the attention logits), and each Value as centre +
+// dequantized residual ([digest], QSAC paragraph, QVG scheme).  The logits are
+// the Query-Key dot products ([abstract]); the output is their softmax-weighted
+// sum of Values.
+//
+// Design:
+//  * 8 waves and 256 queries per workgroup (32 per wave, lane = query), one
+//    workgroup per CU.  All 8 waves share the rebuild of each 64-key tile.
+//  * Two LDS buffers.  While the waves run the MFMAs of tile j from one buffer,
+//    every thread rebuilds its share of tile j+1 into the other from registers
+//    that were loaded one tile ahead; the centre indices are loaded two tiles
+//    ahead because they address the centre rows.  One barrier per tile.
+//  * Rebuild by channel pairs.  A pair of 2-bit codes becomes an exact fp16
+//    pair by placing the two fields in the mantissa of 1024.0 and subtracting
+//    1024; mixed-precision FMAs then form centre + z + c s in fp32 and round
+//    each value to fp16 once (7 VALU ops per pair).  Inside each 16-channel
+//    group the channels sit in paired order (position 2j holds channel j,
+//    position 2j+1 channel j+8), which is where one shift of a code word puts
+//    fields j and j+8; queries, centres and U^T use the same order and the
+//    output is written back in channel order.
+//  * V~ is stored row-major like K~ and read with ds_read_b64_tr_b16, which
+//    gives each lane four consecutive keys of one channel: the A operand of
+//    O^T += V~^T P^T, without a transposing store.
+//  * PSAC as 16 extra contraction columns: q.(k_hat + U c_hat) = q.k_hat +
+//    (U^T q).c_hat, with U^T q computed once per workgroup on the MFMA unit.
+//  * Online softmax in base 2 with a lazy running max: it only moves when a
+//    tile's maximum exceeds it by more than 8, so probabilities stay below 2^8
+//    and most tiles skip the rescaling of the accumulators.
+//  * All workgroups of one (head, key range) run on one XCD (workgroups are
+//    dealt to the 8 XCDs round-robin), so their cache reads share its L2.
+#include "qwm_internal.h"
+
+namespace qwm {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s4_t lds_s4;
+
+constexpr int NW = 8;                  // waves per workgroup
+constexpr int NT = 64 * NW;            // threads per workgroup
+constexpr int BM = kAttnBf16Queries;   // queries per workgroup (32 per wave)
+constexpr int BN = 64;                 // keys per tile
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;           // log2 headroom before the running max moves
+static_assert(BM == 32 * NW, "one 32-query block per wave");
+
+struct Grid {
+  int n_qb;     // query blocks per head
+  int qpb;      // queries per block: a multiple of 32, at most BM
+  int heads;
+  int total;    // n_qb * heads * splits
+  int per_xcd;  // ceil(total / 8)
+};
+
+__device__ __forceinline__ h2_t as_h2(uint32_t x) { return __builtin_bit_cast(h2_t, x); }
+__device__ __forceinline__ uint32_t as_u32(h2_t x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ _Float16 bf_to_h(uint32_t bits) { return (_Float16)__uint_as_float(bits << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// Position of PSAC column k in the K~ rows (and of U^T q in the Q fragment):
+// the MFMA that computes U^T q leaves columns 4hf..4hf+3 and 8+4hf..8+4hf+3 in
+// lane half hf.
+__device__ __forceinline__ int psac_col(int k) { return 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3); }
+
+// One pair of rebuilt values, each rounded to fp16 once:
+//   (mu.lo + (c.lo s + z), mu.hi + (c.hi s + z))
+// c: the exact code pair (fp16), zs: half2 (zero, scale), mu: the centre pair
+// (fp16).  v_fma_mix_f32 forms c s + z in fp32 from the fp16 halves (the
+// product is exact and the fp32 rounding far below fp16's); v_fma_mixlo/hi_f16
+// add the centre and round once into each half of the result.
+__device__ __forceinline__ uint32_t round_pair(uint32_t c, uint32_t zs, uint32_t mu) {
+  float t0, t1;
+  uint32_t r;
+  asm("v_fma_mix_f32 %0, %1, %2, %2 op_sel:[0,1,0] op_sel_hi:[1,1,1]" : "=v"(t0) : "v"(c), "v"(zs));
+  asm("v_fma_mix_f32 %0, %1, %2, %2 op_sel:[1,1,0] op_sel_hi:[1,1,1]" : "=v"(t1) : "v"(c), "v"(zs));
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(mu), "v"(t0));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(mu), "v"(t1));
+  return r;
+}
+
+// 16 values centre + z + code * s of one (token, group) in paired channel
+// order.  w: the group's code word (channel i in bits 2i, 2i+1); zs: half2
+// (zero, scale); m0, m1: the centre's 16 fp16 values in paired order.  Codes j
+// and j+8 of one shift land in the low bits of each half; or-ing them into the
+// mantissa of 1024.0 (ulp 1) and subtracting 1024 gives them exactly as fp16.
+__device__ __forceinline__ void rebuild16(uint32_t w, uint32_t zs, const uint4& m0, const uint4& m1, uint4& o0,
+                                          uint4& o1, uint32_t magic_v, uint32_t mask_s) {
+  const h2_t magic = as_h2(0x64006400u);  // (1024, 1024)
+  const uint32_t mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+  uint32_t r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t x;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(w >> (2 * j)), "s"(mask_s), "v"(magic_v));
+    r[j] = round_pair(as_u32(as_h2(x) - magic), zs, mu[j]);
+  }
+  o0 = make_uint4(r[0], r[1], r[2], r[3]);
+  o1 = make_uint4(r[4], r[5], r[6], r[7]);
+}
+
+template <int D, bool PS>
+__global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr) {
+  constexpr int NG = D / 16;
+  constexpr int NKS = NG + (PS ? 1 : 0);  // MFMA k-steps of S (last: PSAC columns)
+  constexpr int KROW = D + 24;            // fp16 pitch of K~ rows: d channels, 16 PSAC columns, 8 pad
+  constexpr int VROW = D + 32;            // fp16 pitch of V~ rows
+  constexpr int KT = BN * KROW;
+  constexpr int BUF = KT + BN * VROW;
+  constexpr int NDB = D / 32;             // 32-row blocks of O^T
+  constexpr int ITEMS = BN * NG;          // (key, group) rebuild items per tensor
+  constexpr int IPT = 2 * ITEMS / NT;     // items per thread
+  static_assert(IPT * NT == 2 * ITEMS && (IPT == 1 || IPT == 2), "rebuild split");
+  static_assert(NT == BN * 8, "one PSAC column pair per thread");
+  __shared__ __align__(16) _Float16 lds[2 * BUF];
+
+  const int bid = blockIdx.x;
+  const int wg = (bid & 7) * gr.per_xcd + (bid >> 3);
+  if (wg >= gr.total) return;
+  const int qb = wg % gr.n_qb;
+  const int hs = wg / gr.n_qb;
+  const int h = hs % gr.heads;
+  const int split = hs / gr.heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int q0 = qb * gr.qpb + wave * 32;
+  const bool wave_active = wave * 32 < gr.qpb && q0 < p.n_q;  // wave-uniform
+  const int qi = q0 + l32;
+  const bool qvalid = wave_active && qi < p.n_q;
+  const int kbeg = split * p.keys_per_split;
+  const int kend = min(p.n_k, kbeg + p.keys_per_split);
+  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+
+  // ---- Q fragment [q | U^T q] in fp16, paired channel order ----
+  h8_t qf[NKS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)h * p.q_head_stride +
+                           (int64_t)(qvalid ? qi : 0) * p.q_token_stride;
+#pragma unroll
+    for (int ks = 0; ks < NG; ++ks) {
+      uint2 a = make_uint2(0u, 0u), b = make_uint2(0u, 0u);
+      if (qvalid) {
+        a = *reinterpret_cast<const uint2*>(qrow + 16 * ks + 4 * hf);
+        b = *reinterpret_cast<const uint2*>(qrow + 16 * ks + 8 + 4 * hf);
+      }
+      qf[ks] = h8_t{bf_to_h(a.x & 0xffffu), bf_to_h(b.x & 0xffffu), bf_to_h(a.x >> 16), bf_to_h(b.x >> 16),
+                    bf_to_h(a.y & 0xffffu), bf_to_h(b.y & 0xffffu), bf_to_h(a.y >> 16), bf_to_h(b.y >> 16)};
+    }
+    if constexpr (PS) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      const uint16_t* ut = p.ut16 + (int64_t)h * 16 * D;
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        h8_t a;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = (_Float16)0.f;
+        if (l32 < 16) a = *reinterpret_cast<const h8_t*>(ut + l32 * D + 16 * ks + 8 * hf);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[NG][i] = (_Float16)acc[i];
+    }
+  }
+
+  // ---- this thread's rebuild items ----
+  bool it_v[IPT];
+  int it_key[IPT], it_g[IPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    if constexpr (IPT == 2) {
+      it_v[u] = u == 1;
+      it_key[u] = tid / NG;
+      it_g[u] = tid % NG;
+    } else {
+      it_v[u] = tid >= ITEMS;
+      it_key[u] = (tid % ITEMS) / NG;
+      it_g[u] = tid % NG;
+    }
+  }
+  const int pk = tid >> 3;                  // PSAC item: key of the tile,
+  const int ppos = 2 * (tid & 7);           // k-slot pair (ppos, ppos + 1)
+  const int pcol = psac_col(ppos);          // holding columns (pcol, pcol + 1)
+
+  const int64_t hN = (int64_t)h * p.Ncap;
+  const int64_t hP = (int64_t)h * p.Pcap;
+  // keys past the end read the last key of the range (finite data, masked scores)
+  auto slot_of = [&](int key) { return hN + min(key, kend - 1); };
+
+  int idx_a[IPT], idx_b[IPT];
+  uint32_t cw[IPT], zs[IPT], craw = 0;
+  uint4 m0[IPT], m1[IPT];
+
+  auto load_idx = [&](int t0, int (&out)[IPT]) {
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int64_t slot = slot_of(t0 + it_key[u]);
+      const void* ib = it_v[u] ? p.idx_v : p.idx_k;
+      const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
+      const int c = bytes == 1 ? (int)static_cast<const uint8_t*>(ib)[slot] : (int)static_cast<const uint16_t*>(ib)[slot];
+      out[u] = min(c, (it_v[u] ? p.C_v : p.C_k) - 1);
+    }
+  };
+  auto load_raw = [&](int t0, const int (&idx)[IPT]) {
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int key = min(t0 + it_key[u], kend - 1);
+      const int64_t slot = hN + key;
+      const uint32_t fr = ((uint32_t)key + __umulhi((uint32_t)key, p.divF_lo)) >> p.divF_s;
+      const int tt = (int)fr * p.tpf + ((key - (int)fr * p.F) >> p.log2T);
+      const int g = it_g[u];
+      cw[u] = (it_v[u] ? p.codes_v : p.codes_k)[slot * NG + g];
+      zs[u] = (it_v[u] ? p.params_v : p.params_k)[(hP + tt) * NG + g];
+      const uint16_t* mrow = it_v[u] ? p.mu_v16 + ((int64_t)h * p.C_v + idx[u]) * D
+                                     : p.mu_k16 + ((int64_t)h * p.C_k + idx[u]) * D;
+      const uint4* m = reinterpret_cast<const uint4*>(mrow + 16 * g);
+      m0[u] = m[0];
+      m1[u] = m[1];
+    }
+    if constexpr (PS) {
+      const int64_t slot = slot_of(t0 + pk);
+      const int8_t* cf = p.coef + slot * p.r;
+      const uint32_t c0 = pcol < p.r ? (uint8_t)cf[pcol] : 0u;
+      const uint32_t c1 = pcol + 1 < p.r ? (uint8_t)cf[pcol + 1] : 0u;
+      craw = c0 | (c1 << 8) | ((uint32_t)p.coef_scale[slot] << 16);
+    }
+  };
+  const uint32_t magic_v = 0x64006400u;  // kept in a VGPR, the mask in an SGPR (one constant-bus read)
+  const uint32_t mask_s = 0x00030003u;
+  auto rebuild = [&](int buf) {
+    _Float16* base = lds + buf * BUF;
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      uint4 o0, o1;
+      rebuild16(cw[u], zs[u], m0[u], m1[u], o0, o1, magic_v, mask_s);
+      _Float16* dst = it_v[u] ? base + KT + it_key[u] * VROW + 16 * it_g[u] : base + it_key[u] * KROW + 16 * it_g[u];
+      reinterpret_cast<uint4*>(dst)[0] = o0;
+      reinterpret_cast<uint4*>(dst)[1] = o1;
+    }
+    if constexpr (PS) {
+      const float sg = (float)__builtin_bit_cast(_Float16, (uint16_t)(craw >> 16));
+      const h2_t c = h2_t{(_Float16)((float)(int8_t)(craw & 0xffu) * sg), (_Float16)((float)(int8_t)((craw >> 8) & 0xffu) * sg)};
+      *reinterpret_cast<h2_t*>(base + pk * KROW + D + ppos) = c;
+    }
+  };
+
+  float m_run = -INFINITY;  // running max, log2 units
+  float l_run = 0.f;        // this lane's share of the sum of probabilities
+  f32x16 o[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
+
+  if (ntiles > 0) {
+    load_idx(kbeg, idx_a);
+    load_raw(kbeg, idx_a);
+    load_idx(kbeg + BN, idx_a);
+    rebuild(0);
+  }
+  __syncthreads();
+
+  const float sl2 = p.scale_log2;
+  const int trow = 4 * hf + ((lane & 15) >> 2);             // transposed read: key row in a 16-key chunk
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // and channel position in a 32-channel block
+  for (int j = 0; j < ntiles; ++j) {
+    const int t0 = kbeg + j * BN;
+    load_raw(t0 + BN, idx_a);       // tile j+1
+    load_idx(t0 + 2 * BN, idx_b);   // tile j+2
+    const _Float16* kt = lds + (j & 1) * BUF;
+    const _Float16* vt = kt + KT;
+    if (wave_active) {
+      // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
+      f32x16 s[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const h8_t a = *reinterpret_cast<const h8_t*>(kt + (32 * mb + l32) * KROW + 16 * ks + 8 * hf);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], s[mb], 0, 0, 0);
+        }
+      }
+      if (t0 + BN > kend) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (t0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3) >= kend) s[mb][i] = -INFINITY;
+      }
+      // ---- online softmax, base 2 ----
+      float mx = s[0][0];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
+        m_run = m_new;
+      }
+      const float moff = -m_run;
+      h8_t pf[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          pf[2 * mb + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, moff));
+      // the sum uses the rounded probabilities that enter P V (exact products, fp32 sum)
+      const h2_t one = h2_t{(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
+      // ---- O^T += V~^T P^T ----
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const _Float16* va = vt + (16 * c + trow) * VROW + 32 * b + tcol;
+          const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va));
+          const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va + 8 * VROW));
+          const h8_t a = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
+        }
+    }
+    rebuild((j + 1) & 1);
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) idx_a[u] = idx_b[u];
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (!qvalid) return;
+  // o[b][4 i4 + t] is stored position sp + t, sp = 32b + 8 i4 + 4hf: channels
+  // ch, ch + 8, ch + 1, ch + 9 with ch = (sp & ~15) + (sp & 15) / 2
+  if (p.splits == 1) {
+    if (p.lse && hf == 0) p.lse[(int64_t)h * p.n_q + qi] = lse;
+    uint16_t* orow = static_cast<uint16_t*>(p.out) + (int64_t)h * p.o_head_stride + (int64_t)qi * p.o_token_stride;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int sp = 32 * b + 8 * i4 + 4 * hf;
+        const int ch = (sp & ~15) + ((sp & 15) >> 1);
+        *reinterpret_cast<uint32_t*>(orow + ch) = pack_bf16(o[b][4 * i4] * inv, o[b][4 * i4 + 2] * inv);
+        *reinterpret_cast<uint32_t*>(orow + ch + 8) = pack_bf16(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
+      }
+  } else {
+    const int64_t pb = ((int64_t)split * gr.heads + h) * p.n_q + qi;
+    if (hf == 0) p.part_ml[pb] = lse;
+    float* prow = p.part_o + pb * D;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int sp = 32 * b + 8 * i4 + 4 * hf;
+        const int ch = (sp & ~15) + ((sp & 15) >> 1);
+        *reinterpret_cast<float2*>(prow + ch) = make_float2(o[b][4 * i4] * inv, o[b][4 * i4 + 2] * inv);
+        *reinterpret_cast<float2*>(prow + ch + 8) = make_float2(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
+      }
+  }
+}
+
+template <int D, bool PS>
+hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
+  Grid g;
+  g.heads = heads;
+  g.n_qb = (p.n_q + BM - 1) / BM;
+  const int per = (p.n_q + g.n_qb - 1) / g.n_qb;  // balance the query blocks
+  g.qpb = (per + 31) / 32 * 32;
+  g.total = g.n_qb * heads * p.splits;
+  g.per_xcd = (g.total + 7) / 8;
+  hipLaunchKernelGGL((attn_bf16_kernel<D, PS>), dim3(g.per_xcd * 8), dim3(NT), 0, stream, p, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream) {
+  hipError_t e;
+  if (head_dim == 128) e = p.r > 0 ? launch_t<128, true>(p, heads, stream) : launch_t<128, false>(p, heads, stream);
+  else e = p.r > 0 ? launch_t<64, true>(p, heads, stream) : launch_t<64, false>(p, heads, stream);
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_combine(p, heads, head_dim, false, stream);
+}
+
+}  // namespace qwm

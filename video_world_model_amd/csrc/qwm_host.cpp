@@ -78,6 +78,9 @@ void fill_layout(const qwm_config* c, qwm_layout_info* L) {
   put(L->norm_k, H * ck * 4);
   put(L->norm_v, H * cv * 4);
   put(L->head_max, H * 4 * 4);
+  put(L->mu_k16, H * ck * D * 2);
+  put(L->mu_v16, H * cv * D * 2);
+  put(L->ut16, H * 16 * D * 2);
   L->calib_bytes = o;
   o = 0;
   const uint64_t N = L->token_capacity, P = L->tile_capacity;
@@ -277,6 +280,28 @@ float bf16_bits_to_f32(uint16_t h) {
 }
 
 int choose_splits(const qwm_config* c, int64_t n_k, int64_t n_q) {
+  if (c->io_dtype == QWM_BF16) {
+    // One 256-query workgroup per CU.  Estimated time: rounds of 256
+    // workgroups times the key tiles each walks (+2 for set-up), plus the
+    // combine pass (launch + partials at about 3 TB/s), in microseconds.
+    const int64_t nqb = (n_q + qwm::kAttnBf16Queries - 1) / qwm::kAttnBf16Queries;
+    const int64_t base = nqb * c->num_heads;
+    const int64_t tiles = std::max<int64_t>(1, (n_k + 63) / 64);
+    const double tile_us = 1.5;
+    int best = 1;
+    double best_t = 1e300;
+    for (int s = 1; s <= 64; ++s) {
+      const int64_t tps = (tiles + s - 1) / s;
+      const int64_t se = (tiles + tps - 1) / tps;
+      if (se != s) continue;
+      if (s > 1 && tps < 4) break;
+      const double rounds = (double)((base * s + 255) / 256);
+      double t = rounds * (tps + 2) * tile_us;
+      if (s > 1) t += 3.0 + (double)s * c->num_heads * n_q * (c->head_dim * 4.0 + 4.0) / 3e6;
+      if (t < best_t) { best_t = t; best = s; }
+    }
+    return best;
+  }
   const int64_t blocks = ((n_q + 127) / 128) * c->num_heads;
   int64_t splits = 1;
   const int64_t target = 1024;  // workgroups to fill 256 CUs several times
@@ -421,6 +446,21 @@ QWM_API int qwm_calib_import(const qwm_config* cfg, void* calib, const float* mu
     hm[h * 4 + 2] = (float)(mv * (1 + 1e-6));
     hm[h * 4 + 3] = 0.f;
   }
+  // fp16 copies for the bf16 attention path, channels of each 16-group in
+  // paired order: position 2j <- channel j, position 2j+1 <- channel j+8
+  auto paired = [](int pos) { return (pos & ~15) + (pos & 15) / 2 + 8 * (pos & 1); };
+  auto f16 = [](double x) { return __builtin_bit_cast(uint16_t, (_Float16)(float)x); };
+  uint16_t* mk16 = reinterpret_cast<uint16_t*>(&blk[L.mu_k16]);
+  uint16_t* mv16 = reinterpret_cast<uint16_t*>(&blk[L.mu_v16]);
+  uint16_t* ut16 = reinterpret_cast<uint16_t*>(&blk[L.ut16]);
+  for (size_t row = 0; row < (size_t)H * ck; ++row)
+    for (int j = 0; j < d; ++j) mk16[row * d + j] = f16(stored(mu_k, row * d + paired(j)));
+  for (size_t row = 0; row < (size_t)H * cv; ++row)
+    for (int j = 0; j < d; ++j) mv16[row * d + j] = f16(stored(mu_v, row * d + paired(j)));
+  for (int h = 0; h < H; ++h)
+    for (int c = 0; c < 16; ++c)
+      for (int j = 0; j < d; ++j)
+        ut16[((size_t)h * 16 + c) * d + j] = c < r ? f16(u[((size_t)h * d + paired(j)) * r + c]) : 0;
   // Blocking copy after draining the caller's stream: the block is complete
   // in device memory when this call returns.
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -621,6 +661,19 @@ int fill_attn(const qwm_config* cfg, const qwm_cache* cache, const void* q, int6
   p.idx_v_bytes = (int)L.idx_v_bytes;
   p.codes_v = reinterpret_cast<const uint32_t*>(cb + L.codes_v);
   p.params_v = reinterpret_cast<const uint32_t*>(cb + L.params_v);
+  p.mu_k16 = reinterpret_cast<const uint16_t*>(kb + L.mu_k16);
+  p.mu_v16 = reinterpret_cast<const uint16_t*>(kb + L.mu_v16);
+  p.ut16 = reinterpret_cast<const uint16_t*>(kb + L.ut16);
+  // key / F = (key + umulhi(key, lo)) >> s with M = 2^32 + lo = ceil(2^(32+s) / F),
+  // s = ceil(log2 F): exact for every key below 2^32 (keys stay below 2^30)
+  int sF = 0;
+  while ((1ll << sF) < cfg->frame_tokens) ++sF;
+  const uint64_t M = ((1ull << (32 + sF)) + (uint64_t)cfg->frame_tokens - 1) / (uint64_t)cfg->frame_tokens;
+  p.divF_lo = (uint32_t)(M - (1ull << 32));
+  p.divF_s = sF;
+  int lt = 0;
+  while ((1 << lt) < cfg->group_tokens) ++lt;
+  p.log2T = lt;
   p.splits = 1;
   p.keys_per_split = std::max(p.n_k, 1);
   return QWM_OK;

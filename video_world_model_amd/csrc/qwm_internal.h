@@ -74,6 +74,14 @@ struct AttnParams {
   const void* idx_v; int idx_v_bytes;
   const uint32_t* codes_v;
   const uint32_t* params_v;
+  // bf16 path: fp16 centres and U^T in paired channel order, and the
+  // frame division key / F = (key + umulhi(key, divF_lo)) >> divF_s
+  const uint16_t* mu_k16;  // [H][C_K][d]
+  const uint16_t* mu_v16;  // [H][C_V][d]
+  const uint16_t* ut16;    // [H][16][d]
+  uint32_t divF_lo;
+  int divF_s;
+  int log2T;
   // outputs
   void* out;
   int64_t o_head_stride, o_token_stride;
@@ -84,13 +92,18 @@ struct AttnParams {
   int splits;            // number of key ranges
   int keys_per_split;    // multiple of the key tile
   float* part_o;         // [splits][H][n_q][d]
-  float* part_ml;        // [splits][H][n_q][2] (max in log2 units, sum)
+  float* part_ml;        // [splits][H][n_q] natural-log lse of each split
 };
 
 QWM_HIDDEN hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io,
                                     bool key, hipStream_t stream);
 QWM_HIDDEN hipError_t launch_attention(const AttnParams& p, int heads, int head_dim, bool f32io,
                                        hipStream_t stream);
+// bf16 activations, softmax attention only (no logits / top-1 export)
+QWM_HIDDEN hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream);
+QWM_HIDDEN hipError_t launch_combine(const AttnParams& p, int heads, int head_dim, bool f32io, hipStream_t stream);
+// queries per workgroup of the bf16 attention kernel
+constexpr int kAttnBf16Queries = 256;
 QWM_HIDDEN hipError_t launch_dense_top1(const void* q, int64_t qhs, int64_t qts, int n_q,
                                         const void* k, int64_t khs, int64_t kts, int n_k,
                                         int heads, int head_dim, bool f32io, int* top1,
