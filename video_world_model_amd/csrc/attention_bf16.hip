@@ -76,17 +76,20 @@ __device__ __forceinline__ int psac_col(int k) { return 8 * ((k >> 2) & 1) + 4 *
 // One pair of rebuilt values, each rounded to fp16 once:
 //   (mu.lo + (c.lo s + z), mu.hi + (c.hi s + z))
 // c: the exact code pair (fp16), zs: half2 (zero, scale), mu: the centre pair
-// (fp16).  v_fma_mix_f32 forms c s + z in fp32 from the fp16 halves (the
-// product is exact and the fp32 rounding far below fp16's); v_fma_mixlo/hi_f16
-// add the centre and round once into each half of the result.
-__device__ __forceinline__ uint32_t round_pair(uint32_t c, uint32_t zs, uint32_t mu) {
-  float t0, t1;
-  uint32_t r;
+// (fp16).  fma_pair: v_fma_mix_f32 forms c s + z in fp32 from the fp16 halves
+// (the product is exact and the fp32 rounding far below fp16's); round_lo/hi:
+// v_fma_mixlo/hi_f16 add the centre and round once into each half.
+__device__ __forceinline__ void fma_pair(uint32_t c, uint32_t zs, float& t0, float& t1) {
   asm("v_fma_mix_f32 %0, %1, %2, %2 op_sel:[0,1,0] op_sel_hi:[1,1,1]" : "=v"(t0) : "v"(c), "v"(zs));
   asm("v_fma_mix_f32 %0, %1, %2, %2 op_sel:[1,1,0] op_sel_hi:[1,1,1]" : "=v"(t1) : "v"(c), "v"(zs));
+}
+__device__ __forceinline__ uint32_t round_lo(uint32_t mu, float t0) {
+  uint32_t r;
   asm("v_fma_mixlo_f16 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(mu), "v"(t0));
-  asm("v_fma_mixhi_f16 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(mu), "v"(t1));
   return r;
+}
+__device__ __forceinline__ void round_hi(uint32_t& r, uint32_t mu, float t1) {
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(mu), "v"(t1));
 }
 
 // 16 values centre + z + code * s of one (token, group) in paired channel
@@ -98,13 +101,21 @@ __device__ __forceinline__ void rebuild16(uint32_t w, uint32_t zs, const uint4& 
                                           uint4& o1, uint32_t magic_v, uint32_t mask_s) {
   const h2_t magic = as_h2(0x64006400u);  // (1024, 1024)
   const uint32_t mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-  uint32_t r[8];
+  uint32_t c[8], r[8];
+  float t0[8], t1[8];
+  // in stages over the 8 pairs, so that no instruction waits on the one before
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t x;
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(w >> (2 * j)), "s"(mask_s), "v"(magic_v));
-    r[j] = round_pair(as_u32(as_h2(x) - magic), zs, mu[j]);
+    c[j] = as_u32(as_h2(x) - magic);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) fma_pair(c[j], zs, t0[j], t1[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = round_lo(mu[j], t0[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) round_hi(r[j], mu[j], t1[j]);
   o0 = make_uint4(r[0], r[1], r[2], r[3]);
   o1 = make_uint4(r[4], r[5], r[6], r[7]);
 }
@@ -198,21 +209,19 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
   // keys past the end read the last key of the range (finite data, masked scores)
   auto slot_of = [&](int key) { return hN + min(key, kend - 1); };
 
-  int idx_a[IPT], idx_b[IPT];
-  uint32_t cw[IPT], zs[IPT], craw = 0;
+  // Compressed-cache fields of one tile for this thread's items; they stream
+  // from HBM, so they are loaded two tiles ahead of their rebuild.  The centre
+  // rows (a small, L2-resident table) are loaded one tile ahead.
+  struct Raw {
+    uint32_t cw[IPT], zs[IPT];
+    int idx[IPT];
+    int8_t pc0, pc1;
+    uint16_t psc;
+  };
+  Raw ra, rb;  // tiles j+1 and j+2
   uint4 m0[IPT], m1[IPT];
 
-  auto load_idx = [&](int t0, int (&out)[IPT]) {
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int64_t slot = slot_of(t0 + it_key[u]);
-      const void* ib = it_v[u] ? p.idx_v : p.idx_k;
-      const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
-      const int c = bytes == 1 ? (int)static_cast<const uint8_t*>(ib)[slot] : (int)static_cast<const uint16_t*>(ib)[slot];
-      out[u] = min(c, (it_v[u] ? p.C_v : p.C_k) - 1);
-    }
-  };
-  auto load_raw = [&](int t0, const int (&idx)[IPT]) {
+  auto load_cache = [&](int t0, Raw& r) {
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const int key = min(t0 + it_key[u], kend - 1);
@@ -220,38 +229,48 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
       const uint32_t fr = ((uint32_t)key + __umulhi((uint32_t)key, p.divF_lo)) >> p.divF_s;
       const int tt = (int)fr * p.tpf + ((key - (int)fr * p.F) >> p.log2T);
       const int g = it_g[u];
-      cw[u] = (it_v[u] ? p.codes_v : p.codes_k)[slot * NG + g];
-      zs[u] = (it_v[u] ? p.params_v : p.params_k)[(hP + tt) * NG + g];
-      const uint16_t* mrow = it_v[u] ? p.mu_v16 + ((int64_t)h * p.C_v + idx[u]) * D
-                                     : p.mu_k16 + ((int64_t)h * p.C_k + idx[u]) * D;
-      const uint4* m = reinterpret_cast<const uint4*>(mrow + 16 * g);
-      m0[u] = m[0];
-      m1[u] = m[1];
+      r.cw[u] = (it_v[u] ? p.codes_v : p.codes_k)[slot * NG + g];
+      r.zs[u] = (it_v[u] ? p.params_v : p.params_k)[(hP + tt) * NG + g];
+      const void* ib = it_v[u] ? p.idx_v : p.idx_k;
+      const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
+      r.idx[u] = bytes == 1 ? (int)static_cast<const uint8_t*>(ib)[slot] : (int)static_cast<const uint16_t*>(ib)[slot];
     }
     if constexpr (PS) {
+      // unconditional loads (columns past the rank are masked at the rebuild),
+      // so that nothing waits for them before the rebuild
       const int64_t slot = slot_of(t0 + pk);
       const int8_t* cf = p.coef + slot * p.r;
-      const uint32_t c0 = pcol < p.r ? (uint8_t)cf[pcol] : 0u;
-      const uint32_t c1 = pcol + 1 < p.r ? (uint8_t)cf[pcol + 1] : 0u;
-      craw = c0 | (c1 << 8) | ((uint32_t)p.coef_scale[slot] << 16);
+      r.pc0 = cf[min(pcol, p.r - 1)];
+      r.pc1 = cf[min(pcol + 1, p.r - 1)];
+      r.psc = p.coef_scale[slot];
+    }
+  };
+  auto load_mu = [&](const Raw& r) {
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int c = min(r.idx[u], (it_v[u] ? p.C_v : p.C_k) - 1);
+      const uint16_t* mrow = it_v[u] ? p.mu_v16 + ((int64_t)h * p.C_v + c) * D : p.mu_k16 + ((int64_t)h * p.C_k + c) * D;
+      const uint4* m = reinterpret_cast<const uint4*>(mrow + 16 * it_g[u]);
+      m0[u] = m[0];
+      m1[u] = m[1];
     }
   };
   const uint32_t magic_v = 0x64006400u;  // kept in a VGPR, the mask in an SGPR (one constant-bus read)
   const uint32_t mask_s = 0x00030003u;
-  auto rebuild = [&](int buf) {
+  auto rebuild = [&](int buf, const Raw& r) {
     _Float16* base = lds + buf * BUF;
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       uint4 o0, o1;
-      rebuild16(cw[u], zs[u], m0[u], m1[u], o0, o1, magic_v, mask_s);
+      rebuild16(r.cw[u], r.zs[u], m0[u], m1[u], o0, o1, magic_v, mask_s);
       _Float16* dst = it_v[u] ? base + KT + it_key[u] * VROW + 16 * it_g[u] : base + it_key[u] * KROW + 16 * it_g[u];
       reinterpret_cast<uint4*>(dst)[0] = o0;
       reinterpret_cast<uint4*>(dst)[1] = o1;
     }
     if constexpr (PS) {
-      const float sg = (float)__builtin_bit_cast(_Float16, (uint16_t)(craw >> 16));
-      const h2_t c = h2_t{(_Float16)((float)(int8_t)(craw & 0xffu) * sg), (_Float16)((float)(int8_t)((craw >> 8) & 0xffu) * sg)};
-      *reinterpret_cast<h2_t*>(base + pk * KROW + D + ppos) = c;
+      const float sg = (float)__builtin_bit_cast(_Float16, r.psc);
+      const float a = pcol < p.r ? (float)r.pc0 : 0.f, b = pcol + 1 < p.r ? (float)r.pc1 : 0.f;
+      *reinterpret_cast<h2_t*>(base + pk * KROW + D + ppos) = h2_t{(_Float16)(a * sg), (_Float16)(b * sg)};
     }
   };
 
@@ -264,10 +283,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
   if (ntiles > 0) {
-    load_idx(kbeg, idx_a);
-    load_raw(kbeg, idx_a);
-    load_idx(kbeg + BN, idx_a);
-    rebuild(0);
+    load_cache(kbeg, ra);
+    load_mu(ra);
+    rebuild(0, ra);
+    load_cache(kbeg + BN, ra);
   }
   __syncthreads();
 
@@ -276,24 +295,31 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // and channel position in a 32-channel block
   for (int j = 0; j < ntiles; ++j) {
     const int t0 = kbeg + j * BN;
-    load_raw(t0 + BN, idx_a);       // tile j+1
-    load_idx(t0 + 2 * BN, idx_b);   // tile j+2
+    load_mu(ra);                    // centre rows of tile j+1
+    load_cache(t0 + 2 * BN, rb);    // cache fields of tile j+2
     const _Float16* kt = lds + (j & 1) * BUF;
     const _Float16* vt = kt + KT;
-    if (wave_active) {
+    if (__builtin_amdgcn_readfirstlane(wave_active)) {
       // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
       f32x16 s[2];
+      const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
-#pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const h8_t a = *reinterpret_cast<const h8_t*>(kt + (32 * mb + l32) * KROW + 16 * ks + 8 * hf);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], s[mb], 0, 0, 0);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? zero16 : s[mb], 0, 0, 0);
         }
       }
-      if (t0 + BN > kend) {
+      // keep four K~ fragments in flight ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NKS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (__builtin_amdgcn_readfirstlane(t0 + BN > kend)) {  // last tile only (uniform)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -330,6 +356,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
+      // rebuild of the next tile into the other buffer: independent VALU work
+      // for the scheduler to place among the P V MFMAs
+      rebuild((j + 1) & 1, ra);
       // ---- O^T += V~^T P^T ----
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -341,10 +370,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
           const h8_t a = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
         }
+    } else {
+      rebuild((j + 1) & 1, ra);
     }
-    rebuild((j + 1) & 1);
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) idx_a[u] = idx_b[u];
+    ra = rb;
     __syncthreads();
   }
 
