@@ -261,7 +261,13 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   const int sidx = half;  // lane = token from here: segment `half`, token l32
   float mylst[L];
 #pragma unroll
-  for (int i = 0; i < L; ++i) mylst[i] = sidx ? lst[1][i] : lst[0][i];
+  for (int i = 0; i < L; ++i) {
+    // both lists pinned in registers first, so the per-lane choice is a
+    // select and not an indexed stack array
+    float a = lst[0][i], b = lst[1][i];
+    asm volatile("" : "+v"(a), "+v"(b));
+    mylst[i] = sidx ? b : a;
+  }
   const int mylen = sidx ? seg_len[1] : seg_len[0];
   const bool valid = l32 < mylen;
   const int first = sidx ? seg_first[1] : seg_first[0];
@@ -423,17 +429,78 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   }
   if (__any(need_band)) {
     reset_best();
+    // Requests (lane t, tracked entry i) are served four at a time by the
+    // whole wave: request q takes lanes 16q..16q+15, each summing CPL channels
+    // of D_c in fp64, then a 16-lane reduction; the owner lane inserts the
+    // result.  The request lists are wave-uniform (scalar), so only the
+    // requests themselves cost work, not every lane of a wave that has one.
+    constexpr int CPL = D / 16;  // channels per lane of a request
+    const int q = lane >> 4, part = lane & 15;
+    const uint32_t tok_bits = (uint32_t)tok_rel;
 #pragma unroll 1
     for (int i = 0; i < L; ++i) {
-      const bool mine = need_band && i >= m_sure && i < a_end;
-      if (!__any(mine)) continue;
-      if (mine) {
-        float key = mylst[0];
+      uint64_t req = __ballot(need_band && i >= m_sure && i < a_end);
+      if (req == 0) continue;
+      float key_i = mylst[0];
 #pragma unroll
-        for (int q = 1; q < L; ++q)
-          if (q == i) key = mylst[q];
-        const int c = (int)(__float_as_uint(key) & mask);
-        if (c < C) insert(exact_d_row(c, load_k16), c);
+      for (int e = 1; e < L; ++e)
+        if (e == i) key_i = mylst[e];
+      const uint32_t c_bits = __float_as_uint(key_i) & mask;
+      while (req) {
+        int tq[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tq[r] = req ? __builtin_ctzll(req) : -1;
+          req &= req ? req - 1 : 0ull;
+        }
+        // this lane's request: owner lane, centre and token row (uniform reads)
+        int my_t = -1, my_c = 0, my_tok = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tq[r];
+          const int cr = t >= 0 ? (int)__builtin_amdgcn_readlane(c_bits, t) : 0;
+          const int kr = t >= 0 ? (int)__builtin_amdgcn_readlane(tok_bits, t) : 0;
+          if (q == r) { my_t = t; my_c = cr; my_tok = kr; }
+        }
+        double part_d = 0.0;
+        if (my_t >= 0 && my_c < C) {
+          const int64_t row = (int64_t)my_tok * p.token_stride + CPL * part;
+          float kv[CPL], mv[CPL];
+          if constexpr (F32IO) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+              kv[j] = static_cast<const float*>(xin)[row + j];
+              mv[j] = static_cast<const float*>(mu_g)[(int64_t)my_c * D + CPL * part + j];
+            }
+          } else {
+            const uint16_t* kp = static_cast<const uint16_t*>(xin) + row;
+            const uint16_t* mp = reinterpret_cast<const uint16_t*>(mu_hi) + my_c * ROW + CPL * part;
+#pragma unroll
+            for (int j = 0; j < CPL; j += 2) {
+              const uint32_t kw2 = *reinterpret_cast<const uint32_t*>(kp + j);
+              const uint32_t mw2 = *reinterpret_cast<const uint32_t*>(mp + j);
+              kv[j] = bf_lo(kw2); kv[j + 1] = bf_hi(kw2);
+              mv[j] = bf_lo(mw2); mv[j + 1] = bf_hi(mw2);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            const double df = F32IO ? (double)kv[j] - (double)mv[j] : (double)(kv[j] - mv[j]);
+            part_d = fma(s64_lds[CPL * part + j] * df, df, part_d);
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) part_d += __shfl_xor(part_d, off);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tq[r];
+          if (t < 0) break;
+          const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)__double_as_longlong(part_d), 16 * r);
+          const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)__double_as_longlong(part_d) >> 32), 16 * r);
+          const double dq = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+          const int cq = (int)(__float_as_uint(key_i) & mask);
+          if (lane == t && cq < C) insert(dq, cq);
+        }
       }
     }
     if (need_band) {
