@@ -95,10 +95,9 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   __bf16* mu_lo = mu_hi + Cpad * ROW;  // used for fp32 activations only
   float* init = reinterpret_cast<float*>(mu_hi + Cpad * ROW * (F32IO ? 2 : 1));
   float* s_lds = init + Cpad;
-  double* s64_lds = reinterpret_cast<double*>(s_lds + D);  // [D] fp64 copy of s
-  double* u_lds = s64_lds + D;                              // [D][rp] fp64 (Keys with PSAC only)
+  double* u_lds = reinterpret_cast<double*>(s_lds + D);  // [D][R] fp64 (Keys with PSAC only)
   // per-wave row buffer for the rare all-centre search (D words per wave)
-  uint32_t* row_lds = reinterpret_cast<uint32_t*>(u_lds + D * 16) + wave * D;
+  uint32_t* row_lds = reinterpret_cast<uint32_t*>(u_lds + D * R) + wave * D;
 
   const void* mu_g = F32IO ? static_cast<const void*>(static_cast<const float*>(p.mu) + (int64_t)h * C * D)
                            : static_cast<const void*>(static_cast<const uint16_t*>(p.mu) + (int64_t)h * C * D);
@@ -128,7 +127,6 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   for (int j = threadIdx.x; j < D; j += 256) {
     const float sj = p.uniform ? 1.f : p.sens[(int64_t)h * D + j];
     s_lds[j] = sj;
-    s64_lds[j] = (double)sj;
   }
   if constexpr (KEY && R > 0)
     for (int e = threadIdx.x; e < D * p.rp; e += 256) u_lds[e] = p.u64[(int64_t)h * D * p.rp + e];
@@ -393,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const double df = F32IO ? (double)k[i] - (double)m[i] : (double)(k[i] - m[i]);
-        dd = fma(s64_lds[16 * g + i] * df, df, dd);
+        dd = fma((double)s_lds[16 * g + i] * df, df, dd);
       }
     }
     return dd;
@@ -486,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
             const double df = F32IO ? (double)kv[j] - (double)mv[j] : (double)(kv[j] - mv[j]);
-            part_d = fma(s64_lds[CPL * part + j] * df, df, part_d);
+            part_d = fma((double)s_lds[CPL * part + j] * df, df, part_d);
           }
         }
 #pragma unroll
@@ -718,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
 
 template <int D, bool F32IO, bool KEY, int KC, int R>
 hipError_t launch_one(const AppendParams& p, int heads, hipStream_t stream) {
-  const size_t lds = append_lds_bytes(p.Cpad, D, F32IO);  // includes room for U
+  const size_t lds = append_lds_bytes(p.Cpad, D, F32IO, R);
   auto fn = append_kernel<D, F32IO, KEY, KC, R>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

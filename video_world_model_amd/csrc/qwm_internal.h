@@ -108,6 +108,6 @@ QWM_HIDDEN hipError_t launch_dense_top1(const void* q, int64_t qhs, int64_t qts,
                                         const void* k, int64_t khs, int64_t kts, int n_k,
                                         int heads, int head_dim, bool f32io, int* top1,
                                         hipStream_t stream);
-QWM_HIDDEN size_t append_lds_bytes(int Cpad, int head_dim, bool f32io);
+QWM_HIDDEN size_t append_lds_bytes(int Cpad, int head_dim, bool f32io, int ucols);
 
 }  // namespace qwm
