@@ -173,8 +173,7 @@ def main():
         reset()
         kk, vv = ks[i % copies], vs[i % copies]
         if e: e[0].record()
-        qwm.append_k(cache, kk)
-        qwm.append_v(cache, vv)
+        qwm.append_kv(cache, kk, vv)
         if e: e[1].record()
         if e: e[2].record()
         qwm.attention(cache, q, out=out, lse=lse, workspace=ws if ws_bytes else None)
@@ -263,8 +262,7 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
     for f in range(w.frames):
         e = ev[f]
         e[0].record()
-        qwm.append_k(cache, ks[0][:, f * F:(f + 1) * F])
-        qwm.append_v(cache, vs[0][:, f * F:(f + 1) * F])
+        qwm.append_kv(cache, ks[0][:, f * F:(f + 1) * F], vs[0][:, f * F:(f + 1) * F])
         e[1].record()
         qwm.attention(cache, q, out=out, lse=lse, workspace=ws)
         e[2].record()

@@ -240,6 +240,15 @@ int qwm_quantize_append_k(const qwm_config* cfg, qwm_cache* cache, const void* k
 int qwm_quantize_append_v(const qwm_config* cfg, qwm_cache* cache, const void* v_new,
                           int64_t n_new, const qwm_strides* st, void* stream);
 
+/* Both appends of the same n_new frames' tokens (Keys k_new with strides
+ * st_k, Values v_new with st_v) in one launch: the same fields, bit for bit,
+ * as qwm_quantize_append_k followed by qwm_quantize_append_v, with twice the
+ * workgroups in flight.  Requires n_k == n_v (else QWM_ERR_STATE); checks both
+ * inputs before launching anything.  Advances n_k and n_v. */
+int qwm_quantize_append_kv(const qwm_config* cfg, qwm_cache* cache, const void* k_new,
+                           const void* v_new, int64_t n_new, const qwm_strides* st_k,
+                           const qwm_strides* st_v, void* stream);
+
 /* Workspace bytes qwm_attention may use for n_q queries over n_tokens cached
  * tokens (split-KV partial results).  0 is always accepted by qwm_attention
  * (then no split is used). */

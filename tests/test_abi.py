@@ -101,9 +101,18 @@ def test_append_error_paths_move_no_counter():
     assert L.qwm_quantize_append_k(ctypes.byref(c), ctypes.byref(h), _fake(0x100002), 880, ctypes.byref(st), None) == qwm.ERR_INVALID_ARG
     bad = qwm.QwmStrides(w.n_tokens * 128, 100)
     assert L.qwm_quantize_append_k(ctypes.byref(c), ctypes.byref(h), _fake(), 880, ctypes.byref(bad), None) == qwm.ERR_INVALID_ARG
+    # fused K+V append: same checks on both inputs, nothing launched on error
+    assert L.qwm_quantize_append_kv(ctypes.byref(c), ctypes.byref(h), _fake(), _fake(), 100, ctypes.byref(st),
+                                    ctypes.byref(st), None) == qwm.ERR_ALIGN
+    assert L.qwm_quantize_append_kv(ctypes.byref(c), ctypes.byref(h), _fake(), _fake(0x100002), 880,
+                                    ctypes.byref(st), ctypes.byref(st), None) == qwm.ERR_INVALID_ARG
+    assert L.qwm_quantize_append_kv(ctypes.byref(c), ctypes.byref(h), _fake(), _fake(), 880, ctypes.byref(st),
+                                    ctypes.byref(bad), None) == qwm.ERR_INVALID_ARG
     assert h.n_k == 0 and h.n_v == 0
-    # K/V imbalance at attention
+    # K/V imbalance at attention and at the fused append
     h.n_k = 880
+    assert L.qwm_quantize_append_kv(ctypes.byref(c), ctypes.byref(h), _fake(), _fake(), 880, ctypes.byref(st),
+                                    ctypes.byref(st), None) == qwm.ERR_STATE
     out_st = qwm.QwmStrides(880 * 128, 128)
     assert L.qwm_attention(ctypes.byref(c), ctypes.byref(h), _fake(), 880, ctypes.byref(st), ctypes.c_float(0),
                            _fake(0x300000), ctypes.byref(out_st), None, None, 0, None) == qwm.ERR_STATE

@@ -185,3 +185,24 @@ def test_split_kv_matches_single_and_empty_cache():
     empty = qwm.Cache(cfg, cache.calib)
     o0, l0 = qwm.attention(empty, q)
     assert float(o0.float().abs().max()) == 0.0 and bool(torch.all(torch.isneginf(l0)))
+
+
+def test_fused_kv_append_equals_separate():
+    import torch
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["lingbot480p"], heads=2, frames=3)
+    cfg = P.cfg_of(w)
+    say("case fused_kv_append")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    c1, calib = P.build_cache(cfg, cal, data["k"], data["v"])
+    c2 = qwm.Cache(cfg, calib)
+    kd, vd = P.to_dev(data["k"], cfg), P.to_dev(data["v"], cfg)
+    F = cfg.frame_tokens
+    qwm.append_kv(c2, kd[:, :F], vd[:, :F])          # one frame, then the rest
+    qwm.append_kv(c2, kd[:, F:], vd[:, F:])
+    torch.cuda.synchronize()
+    assert c2.n_k == c1.n_k and c2.n_v == c1.n_v
+    a1, a2 = c1.arrays(), c2.arrays()
+    for key in a1:
+        assert torch.equal(a1[key], a2[key]), key

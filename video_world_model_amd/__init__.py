@@ -23,7 +23,7 @@ UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE = 1, 2, 3
 
 EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint", "qwm_calibrate_host",
            "qwm_calib_import", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
-           "qwm_quantize_append_v", "qwm_attention_workspace_size", "qwm_attention",
+           "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention",
            "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
 
 
@@ -82,6 +82,7 @@ def lib():
             "qwm_cache_init": (ctypes.c_int, [CFG, P, P, ctypes.POINTER(QwmCache)]),
             "qwm_quantize_append_k": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P]),
             "qwm_quantize_append_v": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P]),
+            "qwm_quantize_append_kv": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, P, I64, ST, ST, P]),
             "qwm_attention_workspace_size": (ctypes.c_size_t, [CFG, I64, I64]),
             "qwm_attention": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, ST, P, P,
                                              ctypes.c_size_t, P]),
@@ -269,6 +270,17 @@ def append_v(cache: Cache, v):
     s = strides(v)
     check(lib().qwm_quantize_append_v(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(v), v.shape[1],
                                       ctypes.byref(s), _stream()))
+
+
+def append_kv(cache: Cache, k, v):
+    """Keys and Values of the same tokens in one launch (same fields as
+    append_k then append_v)."""
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    c = cache.cfg.c()
+    sk, sv = strides(k), strides(v)
+    check(lib().qwm_quantize_append_kv(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(k), _ptr(v), k.shape[1],
+                                       ctypes.byref(sk), ctypes.byref(sv), _stream()))
 
 
 def workspace_bytes(cfg: Config, n_tokens: int, n_q: int) -> int:

@@ -7,6 +7,10 @@ hipError_t launch_append_d64_bf16(const AppendParams& p, int heads, bool key, hi
 hipError_t launch_append_d64_f32(const AppendParams& p, int heads, bool key, hipStream_t stream);
 hipError_t launch_append_d128_bf16(const AppendParams& p, int heads, bool key, hipStream_t stream);
 hipError_t launch_append_d128_f32(const AppendParams& p, int heads, bool key, hipStream_t stream);
+hipError_t launch_append_d64_bf16_kv(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream);
+hipError_t launch_append_d64_f32_kv(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream);
+hipError_t launch_append_d128_bf16_kv(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream);
+hipError_t launch_append_d128_f32_kv(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream);
 
 size_t append_lds_bytes(int Cpad, int head_dim, bool f32io, int ucols) {
   const size_t row = (size_t)(head_dim + 8) * 2;
@@ -22,6 +26,14 @@ hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f3
   if (head_dim == 128) return f32io ? launch_append_d128_f32(p, heads, key, stream)
                                     : launch_append_d128_bf16(p, heads, key, stream);
   return f32io ? launch_append_d64_f32(p, heads, key, stream) : launch_append_d64_bf16(p, heads, key, stream);
+}
+
+hipError_t launch_append_kv(const AppendParams& pk, const AppendParams& pv, int heads, int head_dim, bool f32io,
+                            hipStream_t stream) {
+  if (pk.total_segs == 0) return hipSuccess;
+  if (head_dim == 128) return f32io ? launch_append_d128_f32_kv(pk, pv, heads, stream)
+                                    : launch_append_d128_bf16_kv(pk, pv, heads, stream);
+  return f32io ? launch_append_d64_f32_kv(pk, pv, heads, stream) : launch_append_d64_bf16_kv(pk, pv, heads, stream);
 }
 
 }  // namespace qwm

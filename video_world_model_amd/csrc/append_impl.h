@@ -28,6 +28,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 namespace qwm {
 namespace append_detail {
 
@@ -75,8 +77,9 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)
 }
 
 // Candidate-count buckets compiled: 1 (argmin modes), 4, 8.
+// One workgroup's work: head blockIdx.y, segment block bx.
 template <int D, bool F32IO, bool KEY, int KC, int R>
-__global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
+__device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NG = D / 16;      // residual groups (= MFMA k-steps of 16 channels)
   constexpr int ROW = D + kPad;   // LDS row pitch (bf16 elements)
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
   __syncthreads();
 
   // ---- segments of this wave ----
-  const int seg_base = (blockIdx.x * kAppendWaves + wave) * kSegsPerWave;
+  const int seg_base = (bx * kAppendWaves + wave) * kSegsPerWave;
   int seg_len[kSegsPerWave], seg_first[kSegsPerWave], seg_pos[kSegsPerWave], seg_frame[kSegsPerWave];
 #pragma unroll
   for (int s = 0; s < kSegsPerWave; ++s) {
@@ -712,6 +715,50 @@ __global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
     }
     p.coef_scale[slot] = sgb;
   }
+}
+
+template <int D, bool F32IO, bool KEY, int KC, int R>
+__global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
+  append_body<D, F32IO, KEY, KC, R>(p, blockIdx.x);
+}
+
+// Keys (blockIdx.z == 0) and Values (blockIdx.z == 1) of the same frames in
+// one launch: twice the workgroups in flight for small appends.
+template <int D, bool F32IO, int KC, int R>
+__global__ __launch_bounds__(256, 2) void append_kv_kernel(AppendParams pk, AppendParams pv) {
+  if (blockIdx.z == 0) append_body<D, F32IO, true, KC, R>(pk, blockIdx.x);
+  else append_body<D, F32IO, false, 1, 0>(pv, blockIdx.x);
+}
+
+template <int D, bool F32IO, int KC, int R>
+hipError_t launch_kv(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream) {
+  const size_t lds = std::max(append_lds_bytes(pk.Cpad, D, F32IO, R), append_lds_bytes(pv.Cpad, D, F32IO, 0));
+  auto fn = append_kv_kernel<D, F32IO, KC, R>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((pk.total_segs + kSegsPerBlock - 1) / kSegsPerBlock, heads, 2);
+  hipLaunchKernelGGL(fn, grid, dim3(256), lds, stream, pk, pv);
+  return hipGetLastError();
+}
+
+template <int D, bool F32IO>
+inline hipError_t dispatch_kv_d(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream) {
+  const bool argmin = !pk.use_range || pk.Kc <= 1;
+  const int rb = pk.r == 0 ? 0 : (pk.r <= 8 ? 8 : 16);
+  if (argmin) {
+    if (rb == 0) return launch_kv<D, F32IO, 1, 0>(pk, pv, heads, stream);
+    if (rb == 8) return launch_kv<D, F32IO, 1, 8>(pk, pv, heads, stream);
+    return launch_kv<D, F32IO, 1, 16>(pk, pv, heads, stream);
+  }
+  if (pk.Kc <= 4) {
+    if (rb == 0) return launch_kv<D, F32IO, 4, 0>(pk, pv, heads, stream);
+    if (rb == 8) return launch_kv<D, F32IO, 4, 8>(pk, pv, heads, stream);
+    return launch_kv<D, F32IO, 4, 16>(pk, pv, heads, stream);
+  }
+  if (rb == 0) return launch_kv<D, F32IO, 8, 0>(pk, pv, heads, stream);
+  if (rb == 8) return launch_kv<D, F32IO, 8, 8>(pk, pv, heads, stream);
+  return launch_kv<D, F32IO, 8, 16>(pk, pv, heads, stream);
 }
 
 template <int D, bool F32IO, bool KEY, int KC, int R>

@@ -545,8 +545,11 @@ QWM_API int qwm_cache_init(const qwm_config* cfg, const void* calib, void* base,
 
 namespace {
 
-int append(const qwm_config* cfg, qwm_cache* cache, const void* x, int64_t n_new, const qwm_strides* st, void* stream,
-           bool key) {
+// Checks one append and fills its kernel parameters (n_new > 0 on success
+// with QWM_OK; *empty set when there is nothing to do).
+int fill_append(const qwm_config* cfg, const qwm_cache* cache, const void* x, int64_t n_new, const qwm_strides* st,
+                bool key, qwm::AppendParams& p, bool* empty) {
+  *empty = false;
   int s = check_config(cfg);
   if (s) return s;
   if (!cache || !cache->base || !cache->calib || cache->abi_version != QWM_ABI_VERSION) return QWM_ERR_INVALID_ARG;
@@ -557,11 +560,14 @@ int append(const qwm_config* cfg, qwm_cache* cache, const void* x, int64_t n_new
   const int64_t n0 = key ? cache->n_k : cache->n_v;
   if (n0 < 0 || n0 % cfg->frame_tokens) return QWM_ERR_STATE;
   if (n0 + n_new > (int64_t)L.token_capacity) return QWM_ERR_CAPACITY;
-  if (n_new == 0) return QWM_OK;
-  const int F = cfg->frame_tokens, D = cfg->head_dim;
+  if (n_new == 0) {
+    *empty = true;
+    return QWM_OK;
+  }
+  const int F = cfg->frame_tokens;
   unsigned char* cb = static_cast<unsigned char*>(cache->base);
   const unsigned char* kb = static_cast<const unsigned char*>(cache->calib);
-  qwm::AppendParams p{};
+  p = qwm::AppendParams{};
   p.x = x;
   p.head_stride = st->head;
   p.token_stride = st->token;
@@ -610,7 +616,15 @@ int append(const qwm_config* cfg, qwm_cache* cache, const void* x, int64_t n_new
   p.rp = rpitch(cfg->rank);
   p.sgroup = reinterpret_cast<const double*>(kb + L.sgroup);
   p.head_max = reinterpret_cast<const float*>(kb + L.head_max);
-  (void)D;
+  return QWM_OK;
+}
+
+int append(const qwm_config* cfg, qwm_cache* cache, const void* x, int64_t n_new, const qwm_strides* st, void* stream,
+           bool key) {
+  qwm::AppendParams p;
+  bool empty;
+  int s = fill_append(cfg, cache, x, n_new, st, key, p, &empty);
+  if (s || empty) return s;
   hipError_t e = qwm::launch_append(p, cfg->num_heads, cfg->head_dim, cfg->io_dtype == QWM_F32, key,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
@@ -690,6 +704,24 @@ QWM_API int qwm_quantize_append_k(const qwm_config* cfg, qwm_cache* cache, const
 QWM_API int qwm_quantize_append_v(const qwm_config* cfg, qwm_cache* cache, const void* v_new, int64_t n_new,
                                   const qwm_strides* st, void* stream) {
   return append(cfg, cache, v_new, n_new, st, stream, false);
+}
+
+QWM_API int qwm_quantize_append_kv(const qwm_config* cfg, qwm_cache* cache, const void* k_new, const void* v_new,
+                                   int64_t n_new, const qwm_strides* st_k, const qwm_strides* st_v, void* stream) {
+  if (!cache) return QWM_ERR_INVALID_ARG;
+  if (cache->n_k != cache->n_v) return QWM_ERR_STATE;
+  qwm::AppendParams pk, pv;
+  bool empty_k, empty_v;
+  int s = fill_append(cfg, cache, k_new, n_new, st_k, true, pk, &empty_k);
+  if (s) return s;
+  if ((s = fill_append(cfg, cache, v_new, n_new, st_v, false, pv, &empty_v))) return s;
+  if (empty_k) return QWM_OK;
+  hipError_t e = qwm::launch_append_kv(pk, pv, cfg->num_heads, cfg->head_dim, cfg->io_dtype == QWM_F32,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  cache->n_k += n_new;
+  cache->n_v += n_new;
+  return QWM_OK;
 }
 
 QWM_API size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tokens, int64_t n_q) {

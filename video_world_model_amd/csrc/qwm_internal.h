@@ -97,6 +97,9 @@ struct AttnParams {
 
 QWM_HIDDEN hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io,
                                     bool key, hipStream_t stream);
+// Keys and Values of the same frames in one launch (pk, pv as for launch_append)
+QWM_HIDDEN hipError_t launch_append_kv(const AppendParams& pk, const AppendParams& pv, int heads, int head_dim,
+                                       bool f32io, hipStream_t stream);
 QWM_HIDDEN hipError_t launch_attention(const AttnParams& p, int heads, int head_dim, bool f32io,
                                        hipStream_t stream);
 // bf16 activations, softmax attention only (no logits / top-1 export)
