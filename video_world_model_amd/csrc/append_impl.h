@@ -15,11 +15,14 @@
 //     argmax F = argmin D.  A = 32 centres x 16 channels from LDS, B = 32
 //     tokens x 16 channels from registers; the accumulator starts at
 //     -||mu||_s^2/2.  Lane (t, h) ends with token t's scores of 16 centres per
-//     block; it keeps the top K_c + 1 as float keys whose low bits carry the
-//     centre index (one max + K_c med3 per score), then merges with lane t^32.
-//  2. Certification: |F~ - F| <= eps (bound below).  If the K_c-th and
-//     (K_c+1)-th keys differ by more than 2 eps the candidate set is exact;
-//     otherwise the lane rescores all centres in fp64 (rare).
+//     block; it keeps the top K_c + 4 as float keys whose low bits carry the
+//     centre index (one max + K_c + 3 med3 per score), then merges with lane
+//     t^32.
+//  2. Certification: |F~_c - F_c| <= eps_c (bound below).  If the members'
+//     lower bars clear the outsiders' upper bars the candidate set is exact;
+//     otherwise the uncertain entries are rescored in fp64, four (token,
+//     centre) pairs at a time by the whole wave, or (rare) the wave searches
+//     all centres for the token.
 //  3. Lane = token from here.  QSAC stage 2 scores each candidate's residual
 //     ranges in fp64; the INT2 tile min/max is a butterfly over the T lanes of
 //     a tile; PSAC accumulates c = U^T e in fp64 with U read wave-uniformly.
@@ -247,15 +250,14 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
 
   // ---- 2. certification ----
   // key_c is F~_c with the centre index in its low pb bits.  For every centre
-  //   |key_c - F_c| <= e_abs + r |key_c|,
-  // e_abs = (2 (n + 1) 2^-24 + 2^-17) scale bounds the fp32 accumulation of the
+  //   |key_c - F_c| <= e_c + r |key_c|,
+  // e_c = (2 (n + 1) 2^-24 + 2^-17) scale_c bounds the fp32 accumulation of the
   // n products and the start value in any order at up to one ulp per operation,
   // plus the bf16 hi/lo split of x (and of mu for fp32 inputs);
-  // scale = maxnorm^2 / 2 + ||x||_s maxnorm bounds every summand's magnitude
-  // (Cauchy-Schwarz), and r = 2^(pb-23) is the truncation of the index bits.
-  // lo_bar / hi_bar below are increasing in the key, so the K_c-th and
-  // (K_c+1)-th keys decide the candidate set, and the last tracked key decides
-  // whether the tracked list holds every centre that can still be a candidate.
+  // scale_c = ||mu_c||_s^2 / 2 + ||k||_s ||mu_c||_s bounds every partial sum of
+  // centre c's score (Cauchy-Schwarz), and r = 2^(pb-23) is the truncation of
+  // the index bits.  The candidate set is certain when the weakest tracked
+  // member's lower bar clears the upper bars of all outsiders.
   constexpr int NACC = (kLo ? 2 : 1) * D + (F32IO ? D : 0) + 1;
   const float mx = p.head_max[h * 4 + p.head_max_slot];
   const int kc = p.Kc;
@@ -311,19 +313,34 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   float myksq = 0.f;
 #pragma unroll
   for (int j = 0; j < D; ++j) myksq = fmaf(s_lds[j] * kval(j), kval(j), myksq);
-  const float scale = 0.5f * mx * mx + 1.01f * sqrtf(fmaxf(myksq, 0.f)) * mx;
-  const float e_abs = (2.f * (NACC + 1) * 0x1p-24f + 0x1p-17f) * 1.001f * scale + 1e-30f;
+  // Bars of every tracked entry from its own centre's norm (the nearest centres
+  // are typically far from the largest norm); the untracked centres, whose keys
+  // are at most the last tracked key, are bounded with the head's largest norm
+  // (the upper bar is increasing in the key).
+  const float ecoef = (2.f * (NACC + 1) * 0x1p-24f + 0x1p-17f) * 1.001f;
+  const float xn = 1.01f * sqrtf(fmaxf(myksq, 0.f));
   const float rr = __uint_as_float((uint32_t)(127 + (int)pb - 23) << 23);
-  auto lo_bar = [&](float k) { return k - e_abs - rr * fabsf(k); };
-  auto hi_bar = [&](float k) { return k + e_abs + rr * fabsf(k); };
-  float th = mylst[0], ph = mylst[1];
+  float lo_e[L], hi_e[L];
 #pragma unroll
-  for (int i = 1; i < L; ++i) {
-    if (i == kc - 1) th = mylst[i];
-    if (i == kc) ph = mylst[i];
+  for (int i = 0; i < L; ++i) {
+    const float k = mylst[i];
+    const int ci = min((int)(__float_as_uint(k) & mask), C - 1);
+    const float nh = fmaxf(-init[ci], 0.f);  // ||mu_c||^2 / 2 (weighted for Keys)
+    const float e = ecoef * (nh + xn * sqrtf(2.f * nh) * 1.0001f) + 1e-30f;
+    const bool fin = k > -INFINITY;  // -inf: fewer centres than tracked entries
+    lo_e[i] = fin ? k - e - rr * fabsf(k) : -INFINITY;
+    hi_e[i] = fin ? k + e + rr * fabsf(k) : -INFINITY;
   }
-  const bool certain = (C <= kc) || (hi_bar(ph) < lo_bar(th));
-  const bool list_covers = (C <= L) || (hi_bar(mylst[L - 1]) < lo_bar(th));
+  const float klast = mylst[L - 1];
+  const float u_hi = (C <= L) ? -INFINITY : klast + ecoef * (0.5f * mx * mx + xn * mx) + 1e-30f + rr * fabsf(klast);
+  float H = u_hi, Lmin = INFINITY;  // best outsider's upper bar, weakest member's lower bar
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (i >= kc) H = fmaxf(H, hi_e[i]);
+    else Lmin = fminf(Lmin, lo_e[i]);
+  }
+  const bool certain = (C <= kc) || (Lmin > H);
+  const bool list_covers = u_hi < Lmin;
 
   // ---- 3. lane = token ----
   // The token's channels are re-read per residual group from memory (the row
@@ -417,16 +434,18 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
     }
   };
 
-  // (1) Band rescoring.  Tracked entries whose lower bar clears the upper bar
-  // of the (K_c+1)-th key are surely candidates (a prefix [0, m)); entries whose
-  // upper bar is below the K_c-th key's lower bar are surely not (from index a
-  // on).  Only [m, a) is rescored exactly, for the remaining K_c - m slots.
+  // (1) Band rescoring.  A tracked member (i < K_c) whose lower bar clears every
+  // outsider's upper bar is surely a candidate; a tracked entry whose upper bar
+  // is below every member's lower bar surely is not.  The rest (the band) is
+  // rescored exactly and fills the slots the sure members leave.
   const bool need_band = !certain && list_covers && valid;
-  int m_sure = 0, a_end = 0;
+  uint32_t sure_bits = 0, band_bits = 0;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    if (i < kc && lo_bar(mylst[i]) > hi_bar(ph)) m_sure = i + 1;
-    if (hi_bar(mylst[i]) >= lo_bar(th)) a_end = i + 1;
+    const bool sure = i < kc && lo_e[i] > H;
+    const bool out = i >= kc && hi_e[i] < Lmin;
+    if (sure) sure_bits |= 1u << i;
+    if (!sure && !out && mylst[i] > -INFINITY) band_bits |= 1u << i;
   }
   if (__any(need_band)) {
     reset_best();
@@ -440,7 +459,7 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
     const uint32_t tok_bits = (uint32_t)tok_rel;
 #pragma unroll 1
     for (int i = 0; i < L; ++i) {
-      uint64_t req = __ballot(need_band && i >= m_sure && i < a_end);
+      uint64_t req = __ballot(need_band && ((band_bits >> i) & 1u));
       if (req == 0) continue;
       float key_i = mylst[0];
 #pragma unroll
@@ -505,11 +524,22 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
       }
     }
     if (need_band) {
-      // slots [m_sure, kc) take the exact winners in order
+      // sure members first (in list order), then the exact winners in order
+      int n_sure = 0;
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        if ((sure_bits >> i) & 1u) {
+          const int c = min((int)(__float_as_uint(mylst[i]) & mask), C - 1);
+#pragma unroll
+          for (int q = 0; q < KC; ++q)
+            if (q == n_sure) { cand[q] = c; tieD[q] = -mylst[i]; }
+          ++n_sure;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < KC; ++q) {
-        const int src = q - m_sure;  // rank among the rescored entries
-        if (q >= m_sure && q < kc) {
+        const int src = q - n_sure;  // rank among the rescored entries
+        if (q >= n_sure && q < kc) {
           int c = bc[0];
           double dd = bd[0];
 #pragma unroll
