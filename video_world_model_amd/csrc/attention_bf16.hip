@@ -35,6 +35,8 @@
 //    dealt to the 8 XCDs round-robin), so their cache reads share its L2.
 #include "qwm_internal.h"
 
+#include <algorithm>
+
 namespace qwm {
 namespace {
 
@@ -52,12 +54,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;           // log2 headroom before the running max moves
 static_assert(BM == 32 * NW, "one 32-query block per wave");
 
+// Work decomposition (stream-K).  The work units are (head, query block, key
+// tile), tile fastest.  Workgroup w takes units [w U / G, (w+1) U / G); a run
+// of units inside one (head, query block) pair is a segment.  A pair cut by a
+// workgroup boundary leaves partial results (O normalised by its own sum, and
+// lse) in workspace slots: slot 2w for workgroup w's first segment, 2w+1 for
+// its last; the combine kernel merges them.  Without a workspace, G equals the
+// number of pairs and every workgroup takes one whole pair.
 struct Grid {
-  int n_qb;     // query blocks per head
-  int qpb;      // queries per block: a multiple of 32, at most BM
+  int n_qb;        // query blocks per head
+  int qpb;         // queries per block: a multiple of 32, at most BM
   int heads;
-  int total;    // n_qb * heads * splits
-  int per_xcd;  // ceil(total / 8)
+  int ntiles;      // key tiles of the cache
+  long long units; // heads * n_qb * ntiles
+  int G;           // workgroups with work
+  int per_xcd;     // ceil(G / 8): workgroups w of one XCD take a contiguous run
 };
 
 __device__ __forceinline__ h2_t as_h2(uint32_t x) { return __builtin_bit_cast(h2_t, x); }
@@ -120,8 +131,11 @@ __device__ __forceinline__ void rebuild16(uint32_t w, uint32_t zs, const uint4& 
   o1 = make_uint4(r[4], r[5], r[6], r[7]);
 }
 
+// One segment: pair (head, query block), key tiles [tb, te).  slot < 0: the
+// segment covers the pair's whole key range (final output), else partial.
 template <int D, bool PS>
-__global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr) {
+__device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, _Float16* lds, int pair, int tb,
+                                               int te, int slot) {
   constexpr int NG = D / 16;
   constexpr int NKS = NG + (PS ? 1 : 0);  // MFMA k-steps of S (last: PSAC columns)
   constexpr int KROW = D + 24;            // fp16 pitch of K~ rows: d channels, 16 PSAC columns, 8 pad
@@ -133,24 +147,18 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
   constexpr int IPT = 2 * ITEMS / NT;     // items per thread
   static_assert(IPT * NT == 2 * ITEMS && (IPT == 1 || IPT == 2), "rebuild split");
   static_assert(NT == BN * 8, "one PSAC column pair per thread");
-  __shared__ __align__(16) _Float16 lds[2 * BUF];
 
-  const int bid = blockIdx.x;
-  const int wg = (bid & 7) * gr.per_xcd + (bid >> 3);
-  if (wg >= gr.total) return;
-  const int qb = wg % gr.n_qb;
-  const int hs = wg / gr.n_qb;
-  const int h = hs % gr.heads;
-  const int split = hs / gr.heads;
+  const int qb = pair % gr.n_qb;
+  const int h = pair / gr.n_qb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
   const int q0 = qb * gr.qpb + wave * 32;
   const bool wave_active = wave * 32 < gr.qpb && q0 < p.n_q;  // wave-uniform
   const int qi = q0 + l32;
   const bool qvalid = wave_active && qi < p.n_q;
-  const int kbeg = split * p.keys_per_split;
-  const int kend = min(p.n_k, kbeg + p.keys_per_split);
-  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  const int kbeg = tb * BN;
+  const int kend = min(p.n_k, te * BN);
+  const int ntiles = te - tb;
 
   // ---- Q fragment [q | U^T q] in fp16, paired channel order ----
   h8_t qf[NKS];
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
   if (!qvalid) return;
   // o[b][4 i4 + t] is stored position sp + t, sp = 32b + 8 i4 + 4hf: channels
   // ch, ch + 8, ch + 1, ch + 9 with ch = (sp & ~15) + (sp & 15) / 2
-  if (p.splits == 1) {
+  if (slot < 0) {
     if (p.lse && hf == 0) p.lse[(int64_t)h * p.n_q + qi] = lse;
     uint16_t* orow = static_cast<uint16_t*>(p.out) + (int64_t)h * p.o_head_stride + (int64_t)qi * p.o_token_stride;
 #pragma unroll
@@ -397,7 +405,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
         *reinterpret_cast<uint32_t*>(orow + ch + 8) = pack_bf16(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
       }
   } else {
-    const int64_t pb = ((int64_t)split * gr.heads + h) * p.n_q + qi;
+    const int64_t pb = (int64_t)slot * BM + wave * 32 + l32;
     if (hf == 0) p.part_ml[pb] = lse;
     float* prow = p.part_o + pb * D;
 #pragma unroll
@@ -413,26 +421,116 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
 }
 
 template <int D, bool PS>
-hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
+__global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr) {
+  constexpr int BUF = BN * (D + 24) + BN * (D + 32);
+  __shared__ __align__(16) _Float16 lds[2 * BUF];
+  const int bid = blockIdx.x;
+  const int w = (bid & 7) * gr.per_xcd + (bid >> 3);
+  if (w >= gr.G) return;
+  if (gr.ntiles == 0) {  // empty cache: every pair writes zeros and lse = -inf
+    attend_segment<D, PS>(p, gr, lds, w, 0, 0, -1);
+    return;
+  }
+  const long long u0 = (long long)w * gr.units / gr.G;
+  const long long u1 = (long long)(w + 1) * gr.units / gr.G;
+  long long u = u0;
+  bool first = true;
+  while (u < u1) {
+    const int pair = (int)(u / gr.ntiles);
+    const int tb = (int)(u % gr.ntiles);
+    const int te = (int)min<long long>(gr.ntiles, tb + (u1 - u));
+    const int slot = (tb == 0 && te == gr.ntiles) ? -1 : (first ? 2 * w : 2 * w + 1);
+    attend_segment<D, PS>(p, gr, lds, pair, tb, te, slot);
+    u += te - tb;
+    first = false;
+    __syncthreads();  // the next segment's first rebuild reuses buffer 0
+  }
+}
+
+// Merges the partial results of the pair cut by the workgroup boundary
+// w = blockIdx.x + 1 (only the first boundary inside a pair does the work),
+// rows 8 blockIdx.y .. + 7 of the pair's query block, 32 threads per row:
+// o = sum_c exp(lse_c - M) o_c / sum_c exp(lse_c - M), lse = M + log sum.
+template <int D>
+__global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) {
+  constexpr int CPT = D / 32;  // channels per thread
+  const int w = blockIdx.x + 1;
+  const long long nt = gr.ntiles;
+  const long long ub = (long long)w * gr.units / gr.G;  // first unit of workgroup w
+  if (ub % nt == 0) return;                             // boundary at a pair start
+  const long long pair_u = ub - ub % nt;
+  const long long up = (long long)(w - 1) * gr.units / gr.G;
+  if (up > pair_u) return;  // an earlier boundary inside the same pair combines it
+  const int pair = (int)(ub / nt);
+  const int qb = pair % gr.n_qb, h = pair / gr.n_qb;
+  const int r = blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int rows = min(gr.qpb, p.n_q - qb * gr.qpb);
+  if (r >= rows) return;
+  const int d0 = (threadIdx.x & 31) * CPT;
+  // contributors: w - 1 (the pair is its last segment, or its first when it
+  // starts exactly at the pair), then w, w + 1, ..., v_end - 1, which start
+  // inside the pair (slot 2v: their first segment)
+  const int slot0 = (up == pair_u) ? 2 * (w - 1) : 2 * (w - 1) + 1;
+  int v_end = w;
+  while (v_end < gr.G && (long long)v_end * gr.units / gr.G < pair_u + nt) ++v_end;
+  float M = p.part_ml[(int64_t)slot0 * BM + r];
+  for (int v = w; v < v_end; ++v) M = fmaxf(M, p.part_ml[(int64_t)(2 * v) * BM + r]);
+  float tot = 0.f, acc[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) acc[j] = 0.f;
+  if (M != -INFINITY) {
+    for (int c = -1; c < v_end - w; ++c) {
+      const int64_t pb = (int64_t)(c < 0 ? slot0 : 2 * (w + c)) * BM + r;
+      const float wt = __expf(p.part_ml[pb] - M);
+      tot += wt;
+      const float* src = p.part_o + pb * D + d0;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) acc[j] = fmaf(wt, src[j], acc[j]);
+    }
+  }
+  const int qi = qb * gr.qpb + r;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  __bf16* dst = static_cast<__bf16*>(p.out) + (int64_t)h * p.o_head_stride + (int64_t)qi * p.o_token_stride + d0;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) dst[j] = (__bf16)(acc[j] * inv);
+  if (d0 == 0 && p.lse) p.lse[(int64_t)h * p.n_q + qi] = tot > 0.f ? M + __logf(tot) : -INFINITY;
+}
+
+template <int D, bool PS>
+hipError_t launch_t(const AttnParams& p, int heads, int max_wg, hipStream_t stream) {
   Grid g;
   g.heads = heads;
   g.n_qb = (p.n_q + BM - 1) / BM;
   const int per = (p.n_q + g.n_qb - 1) / g.n_qb;  // balance the query blocks
   g.qpb = (per + 31) / 32 * 32;
-  g.total = g.n_qb * heads * p.splits;
-  g.per_xcd = (g.total + 7) / 8;
+  g.ntiles = (p.n_k + BN - 1) / BN;
+  const long long pairs = (long long)g.n_qb * heads;
+  g.units = pairs * g.ntiles;
+  if (g.ntiles == 0 || !p.part_o) {
+    g.G = (int)pairs;  // one whole pair per workgroup
+  } else if (pairs <= max_wg) {
+    // k equal pieces per pair (at least 4 tiles each): workgroup boundaries
+    // fall on pair boundaries every k workgroups, one segment per workgroup
+    const long long k = std::max<long long>(1, std::min<long long>(max_wg / pairs, g.ntiles / 4));
+    g.G = (int)(pairs * k);
+  } else {
+    g.G = max_wg;  // one workgroup per CU, at most two segments each
+  }
+  g.per_xcd = (g.G + 7) / 8;
   hipLaunchKernelGGL((attn_bf16_kernel<D, PS>), dim3(g.per_xcd * 8), dim3(NT), 0, stream, p, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
+  hipLaunchKernelGGL((combine_sk_kernel<D>), dim3(g.G - 1, (g.qpb + 7) / 8), dim3(256), 0, stream, p, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream) {
-  hipError_t e;
-  if (head_dim == 128) e = p.r > 0 ? launch_t<128, true>(p, heads, stream) : launch_t<128, false>(p, heads, stream);
-  else e = p.r > 0 ? launch_t<64, true>(p, heads, stream) : launch_t<64, false>(p, heads, stream);
-  if (e != hipSuccess || p.splits == 1) return e;
-  return launch_combine(p, heads, head_dim, false, stream);
+  const int max_wg = kAttnBf16MaxWorkgroups;
+  if (head_dim == 128)
+    return p.r > 0 ? launch_t<128, true>(p, heads, max_wg, stream) : launch_t<128, false>(p, heads, max_wg, stream);
+  return p.r > 0 ? launch_t<64, true>(p, heads, max_wg, stream) : launch_t<64, false>(p, heads, max_wg, stream);
 }
 
 }  // namespace qwm

@@ -281,28 +281,6 @@ float bf16_bits_to_f32(uint16_t h) {
 }
 
 int choose_splits(const qwm_config* c, int64_t n_k, int64_t n_q) {
-  if (c->io_dtype == QWM_BF16) {
-    // One 256-query workgroup per CU.  Estimated time: rounds of 256
-    // workgroups times the key tiles each walks (+2 for set-up), plus the
-    // combine pass (launch + partials at about 3 TB/s), in microseconds.
-    const int64_t nqb = (n_q + qwm::kAttnBf16Queries - 1) / qwm::kAttnBf16Queries;
-    const int64_t base = nqb * c->num_heads;
-    const int64_t tiles = std::max<int64_t>(1, (n_k + 63) / 64);
-    const double tile_us = 1.5;
-    int best = 1;
-    double best_t = 1e300;
-    for (int s = 1; s <= 64; ++s) {
-      const int64_t tps = (tiles + s - 1) / s;
-      const int64_t se = (tiles + tps - 1) / tps;
-      if (se != s) continue;
-      if (s > 1 && tps < 4) break;
-      const double rounds = (double)((base * s + 255) / 256);
-      double t = rounds * (tps + 2) * tile_us;
-      if (s > 1) t += 3.0 + (double)s * c->num_heads * n_q * (c->head_dim * 4.0 + 4.0) / 3e6;
-      if (t < best_t) { best_t = t; best = s; }
-    }
-    return best;
-  }
   const int64_t blocks = ((n_q + 127) / 128) * c->num_heads;
   int64_t splits = 1;
   const int64_t target = 1024;  // workgroups to fill 256 CUs several times
@@ -724,8 +702,16 @@ QWM_API int qwm_quantize_append_kv(const qwm_config* cfg, qwm_cache* cache, cons
   return QWM_OK;
 }
 
+// Partial-result workspace of the bf16 attention (stream-K): two slots of
+// kAttnBf16Queries rows per workgroup, O in fp32 then the lse values.
+size_t bf16_partial_bytes(const qwm_config* cfg) {
+  const size_t slots = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
+  return align256(slots * (size_t)cfg->head_dim * 4) + slots * 4;
+}
+
 QWM_API size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tokens, int64_t n_q) {
   if (check_config(cfg) || n_tokens < 0 || n_q < 0) return 0;
+  if (cfg->io_dtype == QWM_BF16) return (n_tokens > 0 && n_q > 0) ? bf16_partial_bytes(cfg) : 0;
   const int splits = choose_splits(cfg, n_tokens, n_q);
   if (splits <= 1) return 0;
   return (size_t)splits * cfg->num_heads * n_q * ((size_t)cfg->head_dim * 4 + 4) + 256;
@@ -745,6 +731,19 @@ QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const v
   p.o_head_stride = st_out->head;
   p.o_token_stride = st_out->token;
   p.lse = lse;
+  if (cfg->io_dtype == QWM_BF16) {
+    // stream-K partials when the workspace holds them, else one whole
+    // (head, query block) per workgroup
+    if (p.n_k > 0 && ws_bytes >= bf16_partial_bytes(cfg)) {
+      const size_t slots = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
+      p.part_o = static_cast<float*>(workspace);
+      p.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                           align256(slots * (size_t)cfg->head_dim * 4));
+    }
+    hipError_t e = qwm::launch_attention(p, cfg->num_heads, cfg->head_dim, false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return QWM_OK;
+  }
   int splits = choose_splits(cfg, p.n_k, n_q);
   const size_t per_split = (size_t)cfg->num_heads * n_q * ((size_t)cfg->head_dim * 4 + 4);
   while (splits > 1 && (size_t)splits * per_split + 256 > ws_bytes) --splits;

@@ -105,8 +105,11 @@ QWM_HIDDEN hipError_t launch_attention(const AttnParams& p, int heads, int head_
 // bf16 activations, softmax attention only (no logits / top-1 export)
 QWM_HIDDEN hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream);
 QWM_HIDDEN hipError_t launch_combine(const AttnParams& p, int heads, int head_dim, bool f32io, hipStream_t stream);
-// queries per workgroup of the bf16 attention kernel
+// queries per workgroup of the bf16 attention kernel, and its workgroup cap
+// (one per CU of the MI355X); the partial-result workspace holds two slots of
+// kAttnBf16Queries rows per workgroup
 constexpr int kAttnBf16Queries = 256;
+constexpr int kAttnBf16MaxWorkgroups = 256;
 QWM_HIDDEN hipError_t launch_dense_top1(const void* q, int64_t qhs, int64_t qts, int n_q,
                                         const void* k, int64_t khs, int64_t kts, int n_k,
                                         int heads, int head_dim, bool f32io, int* top1,
