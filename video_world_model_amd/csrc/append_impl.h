@@ -81,8 +81,9 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)
 
 // Candidate-count buckets compiled: 1 (argmin modes), 4, 8.
 // One workgroup's work: head blockIdx.y, segment block bx.
-template <int D, bool F32IO, bool KEY, int KC, int R>
+template <int D, bool F32IO, bool KEY, int KC, int R, int NW>
 __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
+  constexpr int NTH = 64 * NW;  // threads per workgroup
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NG = D / 16;      // residual groups (= MFMA k-steps of 16 channels)
   constexpr int ROW = D + kPad;   // LDS row pitch (bf16 elements)
@@ -109,7 +110,7 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
                            : static_cast<const void*>(static_cast<const uint16_t*>(p.mu) + (int64_t)h * C * D);
 
   // ---- stage the codebook, the accumulator start values and s in LDS ----
-  for (int e = threadIdx.x; e < Cpad * NV; e += 256) {
+  for (int e = threadIdx.x; e < Cpad * NV; e += NTH) {
     const int c = e / NV, j8 = (e % NV) * 8;
     if constexpr (F32IO) {
       float v[8];
@@ -128,18 +129,18 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
       *reinterpret_cast<uint4*>(mu_hi + c * ROW + j8) = w;
     }
   }
-  for (int c = threadIdx.x; c < Cpad; c += 256)
+  for (int c = threadIdx.x; c < Cpad; c += NTH)
     init[c] = c < C ? -p.norm_half[(int64_t)h * C + c] : -3.0e38f;
-  for (int j = threadIdx.x; j < D; j += 256) {
+  for (int j = threadIdx.x; j < D; j += NTH) {
     const float sj = p.uniform ? 1.f : p.sens[(int64_t)h * D + j];
     s_lds[j] = sj;
   }
   if constexpr (KEY && R > 0)
-    for (int e = threadIdx.x; e < D * p.rp; e += 256) u_lds[e] = p.u64[(int64_t)h * D * p.rp + e];
+    for (int e = threadIdx.x; e < D * p.rp; e += NTH) u_lds[e] = p.u64[(int64_t)h * D * p.rp + e];
   __syncthreads();
 
   // ---- segments of this wave ----
-  const int seg_base = (bx * kAppendWaves + wave) * kSegsPerWave;
+  const int seg_base = (bx * NW + wave) * kSegsPerWave;
   int seg_len[kSegsPerWave], seg_first[kSegsPerWave], seg_pos[kSegsPerWave], seg_frame[kSegsPerWave];
 #pragma unroll
   for (int s = 0; s < kSegsPerWave; ++s) {
@@ -747,29 +748,44 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   }
 }
 
-template <int D, bool F32IO, bool KEY, int KC, int R>
-__global__ __launch_bounds__(256, 2) void append_kernel(AppendParams p) {
-  append_body<D, F32IO, KEY, KC, R>(p, blockIdx.x);
+// Workgroups of 4 waves (two per CU when the codebook leaves room), or of 8
+// waves for large codebooks (one workgroup per CU): 8 waves per CU either way.
+template <int D, bool F32IO, bool KEY, int KC, int R, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void append_kernel(AppendParams p) {
+  append_body<D, F32IO, KEY, KC, R, NW>(p, blockIdx.x);
 }
 
 // Keys (blockIdx.z == 0) and Values (blockIdx.z == 1) of the same frames in
 // one launch: twice the workgroups in flight for small appends.
-template <int D, bool F32IO, int KC, int R>
-__global__ __launch_bounds__(256, 2) void append_kv_kernel(AppendParams pk, AppendParams pv) {
-  if (blockIdx.z == 0) append_body<D, F32IO, true, KC, R>(pk, blockIdx.x);
-  else append_body<D, F32IO, false, 1, 0>(pv, blockIdx.x);
+template <int D, bool F32IO, int KC, int R, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void append_kv_kernel(AppendParams pk, AppendParams pv) {
+  if (blockIdx.z == 0) append_body<D, F32IO, true, KC, R, NW>(pk, blockIdx.x);
+  else append_body<D, F32IO, false, 1, 0, NW>(pv, blockIdx.x);
+}
+
+// 8 waves when a 4-wave workgroup's LDS would not leave room for a second one
+inline int waves_for(int Cpad, int D, bool f32io, int ucols) {
+  return append_lds_bytes(Cpad, D, f32io, ucols, 4) > 80 * 1024 ? 8 : 4;
+}
+
+template <int D, bool F32IO, int KC, int R, int NW>
+hipError_t launch_kv_nw(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream) {
+  const size_t lds = std::max(append_lds_bytes(pk.Cpad, D, F32IO, R, NW), append_lds_bytes(pv.Cpad, D, F32IO, 0, NW));
+  auto fn = append_kv_kernel<D, F32IO, KC, R, NW>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int per_block = NW * kSegsPerWave;
+  dim3 grid((pk.total_segs + per_block - 1) / per_block, heads, 2);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * NW), lds, stream, pk, pv);
+  return hipGetLastError();
 }
 
 template <int D, bool F32IO, int KC, int R>
 hipError_t launch_kv(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream) {
-  const size_t lds = std::max(append_lds_bytes(pk.Cpad, D, F32IO, R), append_lds_bytes(pv.Cpad, D, F32IO, 0));
-  auto fn = append_kv_kernel<D, F32IO, KC, R>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  dim3 grid((pk.total_segs + kSegsPerBlock - 1) / kSegsPerBlock, heads, 2);
-  hipLaunchKernelGGL(fn, grid, dim3(256), lds, stream, pk, pv);
-  return hipGetLastError();
+  const int nw = std::max(waves_for(pk.Cpad, D, F32IO, R), waves_for(pv.Cpad, D, F32IO, 0));
+  return nw == 8 ? launch_kv_nw<D, F32IO, KC, R, 8>(pk, pv, heads, stream)
+                 : launch_kv_nw<D, F32IO, KC, R, 4>(pk, pv, heads, stream);
 }
 
 template <int D, bool F32IO>
@@ -791,16 +807,23 @@ inline hipError_t dispatch_kv_d(const AppendParams& pk, const AppendParams& pv, 
   return launch_kv<D, F32IO, 8, 16>(pk, pv, heads, stream);
 }
 
-template <int D, bool F32IO, bool KEY, int KC, int R>
-hipError_t launch_one(const AppendParams& p, int heads, hipStream_t stream) {
-  const size_t lds = append_lds_bytes(p.Cpad, D, F32IO, R);
-  auto fn = append_kernel<D, F32IO, KEY, KC, R>;
+template <int D, bool F32IO, bool KEY, int KC, int R, int NW>
+hipError_t launch_one_nw(const AppendParams& p, int heads, hipStream_t stream) {
+  const size_t lds = append_lds_bytes(p.Cpad, D, F32IO, R, NW);
+  auto fn = append_kernel<D, F32IO, KEY, KC, R, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid((p.total_segs + kSegsPerBlock - 1) / kSegsPerBlock, heads);
-  hipLaunchKernelGGL(fn, grid, dim3(256), lds, stream, p);
+  const int per_block = NW * kSegsPerWave;
+  dim3 grid((p.total_segs + per_block - 1) / per_block, heads);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * NW), lds, stream, p);
   return hipGetLastError();
+}
+
+template <int D, bool F32IO, bool KEY, int KC, int R>
+hipError_t launch_one(const AppendParams& p, int heads, hipStream_t stream) {
+  return waves_for(p.Cpad, D, F32IO, R) == 8 ? launch_one_nw<D, F32IO, KEY, KC, R, 8>(p, heads, stream)
+                                              : launch_one_nw<D, F32IO, KEY, KC, R, 4>(p, heads, stream);
 }
 
 template <int D, bool F32IO>

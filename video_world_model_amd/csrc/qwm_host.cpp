@@ -51,7 +51,7 @@ int check_config(const qwm_config* c) {
   if (cap > (int64_t)1 << 30) return QWM_ERR_UNSUPPORTED;
   // codebook + start values must fit in LDS (160 KiB per workgroup)
   const int cmax = std::max(c->num_centroids_k, c->num_centroids_v);
-  if (qwm::append_lds_bytes(ceil_div(cmax, 32) * 32, c->head_dim, c->io_dtype == QWM_F32, rpitch(c->rank)) >
+  if (qwm::append_lds_bytes(ceil_div(cmax, 32) * 32, c->head_dim, c->io_dtype == QWM_F32, rpitch(c->rank), 8) >
       160 * 1024)
     return QWM_ERR_UNSUPPORTED;
   return QWM_OK;

@@ -13,9 +13,7 @@ namespace qwm {
 // a multiple of 32 inside the frame.  Parameter tiles (T | 32) never straddle
 // a segment.
 constexpr int kSegTokens = 32;
-constexpr int kAppendWaves = 4;          // waves per workgroup
 constexpr int kSegsPerWave = 2;          // one 32-token MFMA N-block each
-constexpr int kSegsPerBlock = kAppendWaves * kSegsPerWave;
 
 struct AppendParams {
   // input activations [H][n_new][d]
@@ -114,6 +112,6 @@ QWM_HIDDEN hipError_t launch_dense_top1(const void* q, int64_t qhs, int64_t qts,
                                         const void* k, int64_t khs, int64_t kts, int n_k,
                                         int heads, int head_dim, bool f32io, int* top1,
                                         hipStream_t stream);
-QWM_HIDDEN size_t append_lds_bytes(int Cpad, int head_dim, bool f32io, int ucols);
+QWM_HIDDEN size_t append_lds_bytes(int Cpad, int head_dim, bool f32io, int ucols, int waves);
 
 }  // namespace qwm
