@@ -25,9 +25,43 @@ def cfg_of(w, **kw):
     return c
 
 
-def oracle_calibration(w, data, cfg, seed=7, iters=None):
-    return oc.calibrate(data["q_hist"], data["k_hist"], data["v_hist"], cfg.c_k, cfg.c_v, cfg.rank, cfg.io,
-                        seed=seed, iters=w.kmeans_iters if iters is None else iters)
+def oracle_calibration(w, data, cfg, seed=7, iters=None, threads=1):
+    """The oracle's calibration of every head (heads are independent; with
+    threads > 1 they are computed in a thread pool and stacked in order)."""
+    it = w.kmeans_iters if iters is None else iters
+    H = data["q_hist"].shape[0]
+    if threads <= 1 or H == 1:
+        return oc.calibrate(data["q_hist"], data["k_hist"], data["v_hist"], cfg.c_k, cfg.c_v, cfg.rank, cfg.io,
+                            seed=seed, iters=it)
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(h):
+        # the oracle seeds head h's k-means with seed + 2h (+1 for Values)
+        c = oc.calibrate(data["q_hist"][h:h + 1], data["k_hist"][h:h + 1], data["v_hist"][h:h + 1], cfg.c_k,
+                         cfg.c_v, cfg.rank, cfg.io, seed=seed + 2 * h, iters=it)
+        return c
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(one, range(H)))
+    return {k: (np.concatenate([pt[k] for pt in parts]) if isinstance(parts[0][k], np.ndarray) else parts[0][k])
+            for k in parts[0]}
+
+
+def check_attention(cfg, cal, h, ko, vo, qh, o, lse):
+    """Attention of queries qh of head h against the oracle: returns the worst
+    output error over its bound and the worst lse error over its bound.
+    Output bound: 2e-2 covers the computation for channels up to |v~| ~ 41;
+    the fp16 contraction's own bound 2^-11 max_t |v~_tj| takes over above
+    that, and a bf16 output adds its storage rounding (half an ulp of |o|).
+    lse is a smooth maximum of the logits (|dlse| <= max_t |dl_t|), so it
+    inherits the logit bound 1e-3 tau ||q|| max_t ||k~_t||."""
+    oo, ll, kr, vr = oracle_attention(cfg, cal, h, ko, vo, qh)
+    half_ulp = 0.0 if cfg.io == "f32" else bf16_half_ulp(oo)
+    tol = np.maximum(2e-2, 2.0 ** -11 * np.abs(vr).max(axis=0))[None, :]
+    worst_o = float(np.max((np.abs(o - oo) - half_ulp) / tol))
+    ltol = 1e-3 / np.sqrt(cfg.head_dim) * np.linalg.norm(qh.astype(np.float64), axis=1) * \
+        np.linalg.norm(kr, axis=1).max()
+    worst_l = float(np.max(np.abs(lse - ll) / ltol))
+    return worst_o, worst_l
 
 
 def to_dev(x, cfg):
