@@ -46,13 +46,11 @@ typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s4_t lds_s4;
 
-constexpr int NW = 8;                  // waves per workgroup
-constexpr int NT = 64 * NW;            // threads per workgroup
-constexpr int BM = kAttnBf16Queries;   // queries per workgroup (32 per wave)
+constexpr int kWaves = 8;              // waves per workgroup (one workgroup per CU)
 constexpr int BN = 64;                 // keys per tile
+constexpr int kSlotRows = 32 * kWaves;  // partial-result rows per slot (the queries of a workgroup)
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;           // log2 headroom before the running max moves
-static_assert(BM == 32 * NW, "one 32-query block per wave");
 
 // Work decomposition (stream-K).  The work units are (head, query block, key
 // tile), tile fastest.  Workgroup w takes units [w U / G, (w+1) U / G); a run
@@ -133,9 +131,10 @@ __device__ __forceinline__ void rebuild16(uint32_t w, uint32_t zs, const uint4& 
 
 // One segment: pair (head, query block), key tiles [tb, te).  slot < 0: the
 // segment covers the pair's whole key range (final output), else partial.
-template <int D, bool PS>
+template <int D, bool PS, int NW>
 __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, _Float16* lds, int pair, int tb,
                                                int te, int slot) {
+  constexpr int NT = 64 * NW;             // threads per workgroup
   constexpr int NG = D / 16;
   constexpr int NKS = NG + (PS ? 1 : 0);  // MFMA k-steps of S (last: PSAC columns)
   constexpr int KROW = D + 24;            // fp16 pitch of K~ rows: d channels, 16 PSAC columns, 8 pad
@@ -145,8 +144,9 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   constexpr int NDB = D / 32;             // 32-row blocks of O^T
   constexpr int ITEMS = BN * NG;          // (key, group) rebuild items per tensor
   constexpr int IPT = 2 * ITEMS / NT;     // items per thread
-  static_assert(IPT * NT == 2 * ITEMS && (IPT == 1 || IPT == 2), "rebuild split");
-  static_assert(NT == BN * 8, "one PSAC column pair per thread");
+  constexpr int PPT = BN * 8 / NT;        // PSAC column pairs per thread
+  static_assert(IPT * NT == 2 * ITEMS && IPT >= 1 && IPT <= 4, "rebuild split");
+  static_assert(PPT * NT == BN * 8 && PPT >= 1, "PSAC split");
 
   const int qb = pair % gr.n_qb;
   const int h = pair / gr.n_qb;
@@ -198,19 +198,20 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   int it_key[IPT], it_g[IPT];
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
-    if constexpr (IPT == 2) {
-      it_v[u] = u == 1;
-      it_key[u] = tid / NG;
-      it_g[u] = tid % NG;
-    } else {
-      it_v[u] = tid >= ITEMS;
-      it_key[u] = (tid % ITEMS) / NG;
-      it_g[u] = tid % NG;
-    }
+    const int it = tid + u * NT;              // items [0, ITEMS) Keys, [ITEMS, 2 ITEMS) Values
+    it_v[u] = (ITEMS % NT == 0) ? (u * NT >= ITEMS) : (it >= ITEMS);
+    const int local = it % ITEMS;
+    it_key[u] = local / NG;
+    it_g[u] = local % NG;
   }
-  const int pk = tid >> 3;                  // PSAC item: key of the tile,
-  const int ppos = 2 * (tid & 7);           // k-slot pair (ppos, ppos + 1)
-  const int pcol = psac_col(ppos);          // holding columns (pcol, pcol + 1)
+  int pk[PPT], ppos[PPT], pcol[PPT];         // PSAC items: key of the tile, k-slot pair, column pair
+#pragma unroll
+  for (int v = 0; v < PPT; ++v) {
+    const int it = tid + v * NT;
+    pk[v] = it >> 3;
+    ppos[v] = 2 * (it & 7);
+    pcol[v] = psac_col(ppos[v]);
+  }
 
   const int64_t hN = (int64_t)h * p.Ncap;
   const int64_t hP = (int64_t)h * p.Pcap;
@@ -223,8 +224,8 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   struct Raw {
     uint32_t cw[IPT], zs[IPT];
     int idx[IPT];
-    int8_t pc0, pc1;
-    uint16_t psc;
+    int8_t pc0[PPT], pc1[PPT];
+    uint16_t psc[PPT];
   };
   Raw ra, rb;  // tiles j+1 and j+2
   uint4 m0[IPT], m1[IPT];
@@ -246,11 +247,14 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     if constexpr (PS) {
       // unconditional loads (columns past the rank are masked at the rebuild),
       // so that nothing waits for them before the rebuild
-      const int64_t slot = slot_of(t0 + pk);
-      const int8_t* cf = p.coef + slot * p.r;
-      r.pc0 = cf[min(pcol, p.r - 1)];
-      r.pc1 = cf[min(pcol + 1, p.r - 1)];
-      r.psc = p.coef_scale[slot];
+#pragma unroll
+      for (int v = 0; v < PPT; ++v) {
+        const int64_t slot = slot_of(t0 + pk[v]);
+        const int8_t* cf = p.coef + slot * p.r;
+        r.pc0[v] = cf[min(pcol[v], p.r - 1)];
+        r.pc1[v] = cf[min(pcol[v] + 1, p.r - 1)];
+        r.psc[v] = p.coef_scale[slot];
+      }
     }
   };
   auto load_mu = [&](const Raw& r) {
@@ -276,9 +280,12 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       reinterpret_cast<uint4*>(dst)[1] = o1;
     }
     if constexpr (PS) {
-      const float sg = (float)__builtin_bit_cast(_Float16, r.psc);
-      const float a = pcol < p.r ? (float)r.pc0 : 0.f, b = pcol + 1 < p.r ? (float)r.pc1 : 0.f;
-      *reinterpret_cast<h2_t*>(base + pk * KROW + D + ppos) = h2_t{(_Float16)(a * sg), (_Float16)(b * sg)};
+#pragma unroll
+      for (int v = 0; v < PPT; ++v) {
+        const float sg = (float)__builtin_bit_cast(_Float16, r.psc[v]);
+        const float a = pcol[v] < p.r ? (float)r.pc0[v] : 0.f, b = pcol[v] + 1 < p.r ? (float)r.pc1[v] : 0.f;
+        *reinterpret_cast<h2_t*>(base + pk[v] * KROW + D + ppos[v]) = h2_t{(_Float16)(a * sg), (_Float16)(b * sg)};
+      }
     }
   };
 
@@ -405,7 +412,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         *reinterpret_cast<uint32_t*>(orow + ch + 8) = pack_bf16(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
       }
   } else {
-    const int64_t pb = (int64_t)slot * BM + wave * 32 + l32;
+    const int64_t pb = (int64_t)slot * kSlotRows + wave * 32 + l32;
     if (hf == 0) p.part_ml[pb] = lse;
     float* prow = p.part_o + pb * D;
 #pragma unroll
@@ -420,15 +427,15 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   }
 }
 
-template <int D, bool PS>
-__global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr) {
+template <int D, bool PS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p, Grid gr) {
   constexpr int BUF = BN * (D + 24) + BN * (D + 32);
   __shared__ __align__(16) _Float16 lds[2 * BUF];
   const int bid = blockIdx.x;
   const int w = (bid & 7) * gr.per_xcd + (bid >> 3);
   if (w >= gr.G) return;
   if (gr.ntiles == 0) {  // empty cache: every pair writes zeros and lse = -inf
-    attend_segment<D, PS>(p, gr, lds, w, 0, 0, -1);
+    attend_segment<D, PS, NW>(p, gr, lds, w, 0, 0, -1);
     return;
   }
   const long long u0 = (long long)w * gr.units / gr.G;
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(AttnParams p, Grid gr)
     const int tb = (int)(u % gr.ntiles);
     const int te = (int)min<long long>(gr.ntiles, tb + (u1 - u));
     const int slot = (tb == 0 && te == gr.ntiles) ? -1 : (first ? 2 * w : 2 * w + 1);
-    attend_segment<D, PS>(p, gr, lds, pair, tb, te, slot);
+    attend_segment<D, PS, NW>(p, gr, lds, pair, tb, te, slot);
     u += te - tb;
     first = false;
     __syncthreads();  // the next segment's first rebuild reuses buffer 0
@@ -473,14 +480,14 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) 
   const int slot0 = (up == pair_u) ? 2 * (w - 1) : 2 * (w - 1) + 1;
   int v_end = w;
   while (v_end < gr.G && (long long)v_end * gr.units / gr.G < pair_u + nt) ++v_end;
-  float M = p.part_ml[(int64_t)slot0 * BM + r];
-  for (int v = w; v < v_end; ++v) M = fmaxf(M, p.part_ml[(int64_t)(2 * v) * BM + r]);
+  float M = p.part_ml[(int64_t)slot0 * kSlotRows + r];
+  for (int v = w; v < v_end; ++v) M = fmaxf(M, p.part_ml[(int64_t)(2 * v) * kSlotRows + r]);
   float tot = 0.f, acc[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) acc[j] = 0.f;
   if (M != -INFINITY) {
     for (int c = -1; c < v_end - w; ++c) {
-      const int64_t pb = (int64_t)(c < 0 ? slot0 : 2 * (w + c)) * BM + r;
+      const int64_t pb = (int64_t)(c < 0 ? slot0 : 2 * (w + c)) * kSlotRows + r;
       const float wt = __expf(p.part_ml[pb] - M);
       tot += wt;
       const float* src = p.part_o + pb * D + d0;
@@ -497,7 +504,9 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) 
 }
 
 template <int D, bool PS>
-hipError_t launch_t(const AttnParams& p, int heads, int max_wg, hipStream_t stream) {
+hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
+  constexpr int BM = 32 * kWaves;               // queries per workgroup
+  const int max_wg = kAttnBf16MaxWorkgroups * 8 / kWaves;  // one CU's worth per 8 waves
   Grid g;
   g.heads = heads;
   g.n_qb = (p.n_q + BM - 1) / BM;
@@ -517,7 +526,7 @@ hipError_t launch_t(const AttnParams& p, int heads, int max_wg, hipStream_t stre
     g.G = max_wg;  // one workgroup per CU, at most two segments each
   }
   g.per_xcd = (g.G + 7) / 8;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, PS>), dim3(g.per_xcd * 8), dim3(NT), 0, stream, p, g);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
   hipLaunchKernelGGL((combine_sk_kernel<D>), dim3(g.G - 1, (g.qpb + 7) / 8), dim3(256), 0, stream, p, g);
@@ -527,10 +536,8 @@ hipError_t launch_t(const AttnParams& p, int heads, int max_wg, hipStream_t stre
 }  // namespace
 
 hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream) {
-  const int max_wg = kAttnBf16MaxWorkgroups;
-  if (head_dim == 128)
-    return p.r > 0 ? launch_t<128, true>(p, heads, max_wg, stream) : launch_t<128, false>(p, heads, max_wg, stream);
-  return p.r > 0 ? launch_t<64, true>(p, heads, max_wg, stream) : launch_t<64, false>(p, heads, max_wg, stream);
+  if (head_dim == 128) return p.r > 0 ? launch_t<128, true>(p, heads, stream) : launch_t<128, false>(p, heads, stream);
+  return p.r > 0 ? launch_t<64, true>(p, heads, stream) : launch_t<64, false>(p, heads, stream);
 }
 
 }  // namespace qwm
