@@ -251,8 +251,8 @@ int qwm_quantize_append_kv(const qwm_config* cfg, qwm_cache* cache, const void* 
 
 /* Workspace bytes qwm_attention may use for n_q queries over n_tokens cached
  * tokens: partial results of query blocks whose key range is divided among
- * workgroups (bf16 activations: a fixed 2 x 256 slots of 256 rows, about 68 MB
- * at d = 128; fp32 activations: split-KV partials).  0 is always accepted by
+ * workgroups (bf16 activations: a fixed 2 x 256 slots of 256 rows, fp16, about
+ * 34 MB at d = 128; fp32 activations: split-KV partials).  0 is always accepted by
  * qwm_attention (then every workgroup takes whole query blocks). */
 size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tokens, int64_t n_q);
 

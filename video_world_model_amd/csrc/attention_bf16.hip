@@ -412,17 +412,19 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         *reinterpret_cast<uint32_t*>(orow + ch + 8) = pack_bf16(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
       }
   } else {
+    // partials: O normalised by its own sum, in fp16 (2^-11 relative, far
+    // below the bf16 output's rounding), and the lse in fp32
     const int64_t pb = (int64_t)slot * kSlotRows + wave * 32 + l32;
     if (hf == 0) p.part_ml[pb] = lse;
-    float* prow = p.part_o + pb * D;
+    uint16_t* prow = reinterpret_cast<uint16_t*>(p.part_o) + pb * D;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int sp = 32 * b + 8 * i4 + 4 * hf;
         const int ch = (sp & ~15) + ((sp & 15) >> 1);
-        *reinterpret_cast<float2*>(prow + ch) = make_float2(o[b][4 * i4] * inv, o[b][4 * i4 + 2] * inv);
-        *reinterpret_cast<float2*>(prow + ch + 8) = make_float2(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
+        *reinterpret_cast<uint32_t*>(prow + ch) = as_u32(h2_t{(_Float16)(o[b][4 * i4] * inv), (_Float16)(o[b][4 * i4 + 2] * inv)});
+        *reinterpret_cast<uint32_t*>(prow + ch + 8) = as_u32(h2_t{(_Float16)(o[b][4 * i4 + 1] * inv), (_Float16)(o[b][4 * i4 + 3] * inv)});
       }
   }
 }
@@ -490,9 +492,9 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) 
       const int64_t pb = (int64_t)(c < 0 ? slot0 : 2 * (w + c)) * kSlotRows + r;
       const float wt = __expf(p.part_ml[pb] - M);
       tot += wt;
-      const float* src = p.part_o + pb * D + d0;
+      const _Float16* src = reinterpret_cast<const _Float16*>(p.part_o) + pb * D + d0;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) acc[j] = fmaf(wt, src[j], acc[j]);
+      for (int j = 0; j < CPT; ++j) acc[j] = fmaf(wt, (float)src[j], acc[j]);
     }
   }
   const int qi = qb * gr.qpb + r;

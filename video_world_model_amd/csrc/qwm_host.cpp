@@ -703,10 +703,10 @@ QWM_API int qwm_quantize_append_kv(const qwm_config* cfg, qwm_cache* cache, cons
 }
 
 // Partial-result workspace of the bf16 attention (stream-K): two slots of
-// kAttnBf16Queries rows per workgroup, O in fp32 then the lse values.
+// kAttnBf16Queries rows per workgroup, O in fp16 then the fp32 lse values.
 size_t bf16_partial_bytes(const qwm_config* cfg) {
-  const size_t slots = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
-  return align256(slots * (size_t)cfg->head_dim * 4) + slots * 4;
+  const size_t rows = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
+  return align256(rows * (size_t)cfg->head_dim * 2) + rows * 4;
 }
 
 QWM_API size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tokens, int64_t n_q) {
@@ -735,10 +735,10 @@ QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const v
     // stream-K partials when the workspace holds them, else one whole
     // (head, query block) per workgroup
     if (p.n_k > 0 && ws_bytes >= bf16_partial_bytes(cfg)) {
-      const size_t slots = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
-      p.part_o = static_cast<float*>(workspace);
+      const size_t rows = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
+      p.part_o = static_cast<float*>(workspace);  // holds fp16 rows on this path
       p.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                           align256(slots * (size_t)cfg->head_dim * 4));
+                                           align256(rows * (size_t)cfg->head_dim * 2));
     }
     hipError_t e = qwm::launch_attention(p, cfg->num_heads, cfg->head_dim, false, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);

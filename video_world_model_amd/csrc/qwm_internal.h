@@ -89,8 +89,8 @@ struct AttnParams {
   // split-KV partials
   int splits;            // number of key ranges
   int keys_per_split;    // multiple of the key tile
-  float* part_o;         // [splits][H][n_q][d]
-  float* part_ml;        // [splits][H][n_q] natural-log lse of each split
+  float* part_o;         // [splits][H][n_q][d] fp32 (bf16 path: [slots][rows][d] fp16)
+  float* part_ml;        // [splits][H][n_q] (bf16 path: [slots][rows]) natural-log lse
 };
 
 QWM_HIDDEN hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io,
