@@ -68,10 +68,10 @@ def attn_flops(w, n_q, n_k):
     return 4.0 * n_q * n_k * w.head_dim * w.heads
 
 
-def traffic_from_profiles(config, src_hash):
-    """HBM bytes per attention launch from committed rocprofv3 counter runs,
-    if they were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "attention_%s_traffic.json" % config)
+def traffic_from_profiles(kernel, config, src_hash):
+    """HBM bytes per launch of `kernel` (attention / append) from committed
+    rocprofv3 counter runs, if they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel, config))
     if not os.path.exists(p):
         return None
     try:
@@ -167,7 +167,13 @@ def main():
     if args.config == "minute":
         return rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torch)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # per step: append (one kernel), attention call, attention kernel alone
+    # (events recorded by the library around its main kernel, on its stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for e in ev:
+        for x in e:
+            x.record()  # creates the events the library records into
+    torch.cuda.synchronize()
 
     def step(i, e=None):
         reset()
@@ -176,7 +182,8 @@ def main():
         qwm.append_kv(cache, kk, vv)
         if e: e[1].record()
         if e: e[2].record()
-        qwm.attention(cache, q, out=out, lse=lse, workspace=ws if ws_bytes else None)
+        qwm.attention(cache, q, out=out, lse=lse, workspace=ws if ws_bytes else None,
+                      kernel_events=(e[4], e[5]) if e else None)
         if e: e[3].record()
 
     for i in range(args.warmup):
@@ -190,14 +197,29 @@ def main():
 
     app_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     att_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in range(args.steps)]
+    attk_ms = [ev[i][4].elapsed_time(ev[i][5]) for i in range(args.steps)]
     ms_step = wall * 1e3 / args.steps
     tok_heads = w.n_tokens * w.heads
     app_bytes = tok_heads * append_bytes_per_token_head(w, cfg)
     flops = attn_flops(w, w.n_q, w.n_tokens)
-    app_avg, att_avg = float(np.mean(app_ms)), float(np.mean(att_ms))
-    achieved_tf = flops / (att_avg * 1e-3) / 1e12
+    app_avg, att_avg, attk_avg = float(np.mean(app_ms)), float(np.mean(att_ms)), float(np.mean(attk_ms))
+    achieved_tf = flops / (attk_avg * 1e-3) / 1e12
+    app_gbs = app_bytes / (app_avg * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profiles(args.config, src_hash)
+    # roofline of the dominant kernel: the fused append (HBM-bound) or the
+    # attention kernel (fp16 MFMA), whichever takes longer per step
+    if app_avg > attk_avg:
+        roofline = {"kernel": "append_kv_kernel (quantize-append, Keys and Values)", "bound": "hbm",
+                    "achieved": round(app_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(app_gbs / PEAK_HBM_GBS, 4),
+                    "traffic": traffic_from_profiles("append", args.config, src_hash),
+                    "algorithmic_bytes_per_launch": round(app_bytes), "ms_per_launch": round(app_avg, 4)}
+    else:
+        roofline = {"kernel": "attn_bf16_kernel (dequant-attention)", "bound": "mfma",
+                    "achieved": round(achieved_tf, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved_tf / PEAK_FP16_TFLOPS, 4),
+                    "traffic": traffic_from_profiles("attention", args.config, src_hash),
+                    "algorithmic_flops_per_launch": flops, "ms_per_launch": round(attk_avg, 4)}
 
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
@@ -221,15 +243,14 @@ def main():
                    "input_copies_rotated": copies},
         "append": {"ms": round(app_avg, 4), "ktokens_s": round(w.n_tokens / (app_avg * 1e-3) / 1e3, 3),
                    "token_heads_s": round(tok_heads / (app_avg * 1e-3), 1),
-                   "algorithmic_gbs": round(app_bytes / (app_avg * 1e-3) / 1e9, 2),
-                   "frac_hbm": round(app_bytes / (app_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "algorithmic_gbs": round(app_gbs, 2), "frac_hbm": round(app_gbs / PEAK_HBM_GBS, 4),
                    "bytes_per_token_head": round(append_bytes_per_token_head(w, cfg), 2)},
-        "attention": {"ms": round(att_avg, 4), "tflops": round(achieved_tf, 2),
+        "attention": {"ms": round(att_avg, 4), "kernel_ms": round(attk_avg, 4),
+                      "combine_ms": round(max(att_avg - attk_avg, 0.0), 4), "tflops": round(achieved_tf, 2),
                       "frac_mfma": round(achieved_tf / PEAK_FP16_TFLOPS, 4),
                       "flops_per_launch": flops,
-                      "compressed_cache_gbs": round((stored - 0) / (att_avg * 1e-3) / 1e9, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved_tf / PEAK_FP16_TFLOPS, 4), "traffic": traffic},
+                      "compressed_cache_gbs": round(stored / (attk_avg * 1e-3) / 1e9, 2)},
+        "roofline": roofline,
         "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4),
                         "stored_bytes": stored, "original_bytes": original},
         "top8_energy_mean": round(float(energy.mean()), 4),
@@ -256,15 +277,18 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
     import numpy as np
     F = w.frame_tokens
     reset()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(w.frames)]
-    t0 = time.perf_counter()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(w.frames)]
+    for e in ev:
+        for x in e:
+            x.record()  # creates the events the library records into
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for f in range(w.frames):
         e = ev[f]
         e[0].record()
         qwm.append_kv(cache, ks[0][:, f * F:(f + 1) * F], vs[0][:, f * F:(f + 1) * F])
         e[1].record()
-        qwm.attention(cache, q, out=out, lse=lse, workspace=ws)
+        qwm.attention(cache, q, out=out, lse=lse, workspace=ws, kernel_events=(e[3], e[4]))
         e[2].record()
         if f % 40 == 0:
             print("[bench] rollout frame %d" % f, file=sys.stderr, flush=True)
@@ -272,8 +296,9 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
     wall = time.perf_counter() - t0
     app = np.array([e[0].elapsed_time(e[1]) for e in ev])
     att = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    attk = np.array([e[3].elapsed_time(e[4]) for e in ev])
     flops = np.array([attn_flops(w, w.n_q, (f + 1) * F) for f in range(w.frames)])
-    tf = flops / (att * 1e-3) / 1e12
+    tf = flops / (attk * 1e-3) / 1e12
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
         "metric": METRIC, "value": round(w.n_tokens / wall / 1e3, 3), "unit": "Ktokens/s", "n_gpus": 1,
@@ -285,9 +310,11 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
         "append_ms_median": round(float(np.median(app)), 4),
         "attention_ms_median": round(float(np.median(att)), 4),
         "attention_ms_final": round(float(att[-1]), 4),
+        "attention_kernel_ms_final": round(float(attk[-1]), 4),
         "attention_tflops_final": round(float(tf[-1]), 2),
         "attention_tflops_steady_median": round(float(np.median(tf[len(tf) // 2:])), 2),
-        "roofline": {"bound": "mfma", "achieved": round(float(tf[-1]), 2), "peak": PEAK_FP16_TFLOPS,
+        "roofline": {"kernel": "attn_bf16_kernel (dequant-attention, final step)", "bound": "mfma",
+                     "achieved": round(float(tf[-1]), 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(float(tf[-1]) / PEAK_FP16_TFLOPS, 4), "traffic": None},
         "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4)},
         "cpu_baseline": None,

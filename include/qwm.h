@@ -274,6 +274,15 @@ int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, 
                   const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
                   float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* qwm_attention with two optional HIP events (hipEvent_t, NULL to skip)
+ * recorded on stream immediately before and after the main attention kernel,
+ * so that its duration can be measured apart from the pass that merges
+ * partial results.  Same arguments, results and errors as qwm_attention. */
+int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                        const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
+                        float* lse, void* workspace, size_t ws_bytes, void* stream,
+                        void* ev_kernel_begin, void* ev_kernel_end);
+
 /* The logits l [H][n_q][n_k] fp32 of the same kernel (debug variant), for
  * logit parity checks on small shapes. */
 int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, const void* q,

@@ -23,7 +23,7 @@ UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE = 1, 2, 3
 
 EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint", "qwm_calibrate_host",
            "qwm_calib_import", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
-           "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention",
+           "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention", "qwm_attention_timed",
            "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
 
 
@@ -86,6 +86,8 @@ def lib():
             "qwm_attention_workspace_size": (ctypes.c_size_t, [CFG, I64, I64]),
             "qwm_attention": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, ST, P, P,
                                              ctypes.c_size_t, P]),
+            "qwm_attention_timed": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, ST, P, P,
+                                                   ctypes.c_size_t, P, P, P]),
             "qwm_attention_logits": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, P]),
             "qwm_top1": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P]),
             "qwm_dense_top1": (ctypes.c_int, [CFG, P, I64, ST, P, I64, ST, P, P]),
@@ -288,7 +290,10 @@ def workspace_bytes(cfg: Config, n_tokens: int, n_q: int) -> int:
     return int(lib().qwm_attention_workspace_size(ctypes.byref(c), n_tokens, n_q))
 
 
-def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float = 0.0):
+def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float = 0.0, kernel_events=None):
+    """Attention of q over the cache.  kernel_events: optional pair of
+    torch.cuda.Event (already recorded once, so that they exist) that the
+    library records around the main attention kernel alone."""
     torch = _torch()
     cfg = cache.cfg
     if out is None:
@@ -301,8 +306,16 @@ def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float 
     c = cfg.c()
     sq, so = strides(q), strides(out)
     nb = workspace.numel() if workspace is not None else 0
-    check(lib().qwm_attention(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1], ctypes.byref(sq),
-                              scale, _ptr(out), ctypes.byref(so), _ptr(lse), _ptr(workspace), nb, _stream()))
+    if kernel_events is None:
+        check(lib().qwm_attention(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1],
+                                  ctypes.byref(sq), scale, _ptr(out), ctypes.byref(so), _ptr(lse), _ptr(workspace),
+                                  nb, _stream()))
+    else:
+        e0, e1 = kernel_events
+        check(lib().qwm_attention_timed(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1],
+                                        ctypes.byref(sq), scale, _ptr(out), ctypes.byref(so), _ptr(lse),
+                                        _ptr(workspace), nb, _stream(), ctypes.c_void_p(e0.cuda_event),
+                                        ctypes.c_void_p(e1.cuda_event)))
     return out, lse
 
 

@@ -387,6 +387,10 @@ __global__ __launch_bounds__(D) void combine_kernel(AttnParams p, int heads) {
 template <int D, bool F32IO>
 hipError_t launch_d(const AttnParams& p, int heads, hipStream_t stream) {
   dim3 grid((p.n_q + BM - 1) / BM, heads, p.splits);
+  if (p.ev_begin) {
+    const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(p.ev_begin), stream);
+    if (er != hipSuccess) return er;
+  }
   if (p.top1) {
     hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_TOP1>), grid, dim3(256), 0, stream, p);
   } else if (p.logits) {
@@ -395,6 +399,7 @@ hipError_t launch_d(const AttnParams& p, int heads, hipStream_t stream) {
     hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_ATTN>), grid, dim3(256), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || p.splits == 1 || p.top1 || p.logits) return e;
   return launch_combine(p, heads, D, F32IO, stream);
 }

@@ -528,8 +528,13 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
     g.G = max_wg;  // one workgroup per CU, at most two segments each
   }
   g.per_xcd = (g.G + 7) / 8;
+  if (p.ev_begin) {
+    const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(p.ev_begin), stream);
+    if (er != hipSuccess) return er;
+  }
   hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
   hipLaunchKernelGGL((combine_sk_kernel<D>), dim3(g.G - 1, (g.qpb + 7) / 8), dim3(256), 0, stream, p, g);
   return hipGetLastError();

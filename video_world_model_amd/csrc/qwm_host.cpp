@@ -717,12 +717,15 @@ QWM_API size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tok
   return (size_t)splits * cfg->num_heads * n_q * ((size_t)cfg->head_dim * 4 + 4) + 256;
 }
 
-QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
-                          const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out, float* lse,
-                          void* workspace, size_t ws_bytes, void* stream) {
+QWM_API int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                                const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
+                                float* lse, void* workspace, size_t ws_bytes, void* stream, void* ev_kernel_begin,
+                                void* ev_kernel_end) {
   qwm::AttnParams p;
   int s = fill_attn(cfg, cache, q, n_q, st_q, scale, p);
   if (s) return s;
+  p.ev_begin = ev_kernel_begin;
+  p.ev_end = ev_kernel_end;
   if ((s = check_act(cfg, out, n_q, st_out))) return s;
   if (n_q == 0) return QWM_OK;
   if (lse && !aligned16(lse)) return QWM_ERR_INVALID_ARG;
@@ -761,6 +764,13 @@ QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const v
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return QWM_OK;
+}
+
+QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                          const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  return qwm_attention_timed(cfg, cache, q, n_q, st_q, scale, out, st_out, lse, workspace, ws_bytes, stream, nullptr,
+                             nullptr);
 }
 
 QWM_API int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,

@@ -86,6 +86,10 @@ struct AttnParams {
   float* lse;            // [H][n_q] or null
   float* logits;         // debug [H][n_q][n_k] or null
   int* top1;             // measure [H][n_q] or null
+  // optional HIP events recorded on the stream around the main attention
+  // kernel (its combine pass excluded), for per-kernel timing
+  void* ev_begin;
+  void* ev_end;
   // split-KV partials
   int splits;            // number of key ranges
   int keys_per_split;    // multiple of the key tile
