@@ -6,26 +6,30 @@
 // and PSAC paragraphs; [review] summary, Eq. 7).  The arithmetic of every
 // stored field is the one documented for qwm_quantize_append_k in qwm.h.
 //
-// Work decomposition.  A workgroup (4 waves) serves one head and 8 segments
-// of <= 32 tokens; each segment is a 32-token MFMA N-block.  The head's
-// centre codebook is staged once in LDS (bf16, rows padded by 16 bytes).
+// Work decomposition.  A workgroup (4 or 8 waves) serves one head; each wave
+// takes two segments of <= 32 tokens (one 32-token MFMA N-block each).  The
+// head's centre codebook is staged once in LDS (bf16, rows padded by 16 bytes,
+// C rounded up to pairs of 32-centre blocks).
 //
 //  1. Screen (MFMA, bf16 -> fp32): F_c = x . mu_c - ||mu_c||_s^2 / 2 for all c,
 //     x = s * k split into bf16 hi + lo (Values: x = v, exact in bf16), so
 //     argmax F = argmin D.  A = 32 centres x 16 channels from LDS, B = 32
 //     tokens x 16 channels from registers; the accumulator starts at
 //     -||mu||_s^2/2.  Lane (t, h) ends with token t's scores of 16 centres per
-//     block; it keeps the top K_c + 4 as float keys whose low bits carry the
-//     centre index (one max + K_c + 3 med3 per score), then merges with lane
-//     t^32.
-//  2. Certification: |F~_c - F_c| <= eps_c (bound below).  If the members'
+//     block; it keeps the top K_c + 2 as float keys whose low bits carry the
+//     centre index (one bit-select, K_c + 1 med3 and one max per score).  The
+//     MFMAs of the next block run while the keys of this one are inserted.
+//  2. Lane = token: v_permlane32_swap hands lane t token t of the first segment
+//     and lane t + 32 token t of the second, with both halves of its list and
+//     of ||k||_s^2 (and, for bf16 Values, of its row, kept from the screen).
+//  3. Certification: |F~_c - F_c| <= eps_c (bound below).  If the members'
 //     lower bars clear the outsiders' upper bars the candidate set is exact;
 //     otherwise the uncertain entries are rescored in fp64, four (token,
 //     centre) pairs at a time by the whole wave, or (rare) the wave searches
 //     all centres for the token.
-//  3. Lane = token from here.  QSAC stage 2 scores each candidate's residual
-//     ranges in fp64; the INT2 tile min/max is a butterfly over the T lanes of
-//     a tile; PSAC accumulates c = U^T e in fp64 with U read wave-uniformly.
+//  4. QSAC stage 2 scores the candidates' residual ranges in fp64; the INT2
+//     tile min/max is a DPP butterfly over the T lanes of a tile; PSAC
+//     accumulates c = U^T e in fp64 with U read wave-uniformly.
 #pragma once
 #include "qwm_internal.h"
 
@@ -51,17 +55,20 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return __half2float(__ushort_as_half(b));
 }
 
-// min / max through v_med3 (no NaN canonicalisation; inputs are finite or
-// +-inf by construction)
-__device__ __forceinline__ float fmin_fast(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -INFINITY); }
-__device__ __forceinline__ float fmax_fast(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
-
 // Insert a key into a descending list of L keys (keeps the L largest).
 template <int L>
 __device__ __forceinline__ void topl_insert(float (&l)[L], float x) {
 #pragma unroll
   for (int i = L - 1; i >= 1; --i) l[i] = __builtin_amdgcn_fmed3f(l[i - 1], l[i], x);
-  l[0] = __builtin_amdgcn_fmed3f(l[0], x, INFINITY);  // max without NaN canonicalisation
+  // max(l[0], x) for keys below +FLT_MAX, in one instruction (a med3 against
+  // +inf would become a max with NaN canonicalisation of x)
+  l[0] = __builtin_amdgcn_fmed3f(l[0], x, 0x1.fffffep127f);
+}
+
+// x of another lane of the same row of 16, by a DPP lane pattern
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
 // Eight consecutive io-typed values of a row, as floats.
@@ -87,7 +94,7 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NG = D / 16;      // residual groups (= MFMA k-steps of 16 channels)
   constexpr int ROW = D + kPad;   // LDS row pitch (bf16 elements)
-  constexpr int L = KC + 1 + 3;   // tracked keys: K_c, the next one, and 3 spare for rescoring
+  constexpr int L = KC + 2;       // tracked keys: K_c, the next one and one spare for rescoring
   constexpr int NV = D / 8;       // 8-value chunks per row
 
   const int h = blockIdx.y;
@@ -163,14 +170,28 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   // ---- 1. screen ----
   // Keys screen one segment per pass (x needs hi and lo parts: fewer live
   // registers); Values screen both segments together and share each A
-  // fragment between two MFMAs.
+  // fragment between two MFMAs.  Each pass is software-pipelined: the MFMAs
+  // of centre block b+1 are issued while the keys of block b are inserted.
   constexpr bool kLo = KEY || F32IO;  // x needs a bf16 lo part
   constexpr int SPP = kLo ? 1 : kSegsPerWave;  // segments per screen pass
+  constexpr int RW = D / 4;  // bf16 words of one lane's half row (8 channels per k-step)
   const uint32_t pb = 32 - __builtin_clz((uint32_t)(Cpad - 1));
   const uint32_t mask = (1u << pb) - 1u;
+  const int nblk = Cpad >> 5;  // even: Cpad is a multiple of 64
+  // ~mask held in a VGPR, so the key is one v_and_or_b32 with the uniform index
+  uint32_t keep = ~mask;
+  asm volatile("" : "+v"(keep));
   float lst[kSegsPerWave][L];
+  float ksq[kSegsPerWave];  // this lane's half of ||k||_s^2 (Values: ||v||^2)
+  // bf16 Values keep the half rows (their MFMA operand) for the lane phase;
+  // Keys, whose operand is s * k in hi + lo parts, load the row again
+  constexpr bool kKeepRow = !kLo;
+  uint32_t raw[kSegsPerWave][kKeepRow ? RW : 1];
 #pragma unroll
   for (int pass = 0; pass < kSegsPerWave / SPP; ++pass) {
+    // compiler barrier: s is read from LDS again in each pass rather than kept
+    // in registers across the screen (it emits no instruction)
+    asm volatile("" ::: "memory");
     bf16x8 xh[SPP][NG];
     bf16x8 xl[SPP][kLo ? NG : 1];
 #pragma unroll
@@ -179,37 +200,60 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
       const bool valid = l32 < seg_len[s];
       // rows of invalid lanes are clamped to a real token and zeroed after the load
       const int64_t row = (int64_t)(seg_first[s] + (valid ? l32 : 0)) * p.token_stride;
+      float q = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         const int c0 = 16 * ks + 8 * half;
-        if constexpr (!kLo) {
-          // bf16 Values: the loaded words are the MFMA operand (x = v exactly)
+        float v[8];
+        if constexpr (F32IO) {
+          load8<true>(xin, row + c0, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = valid ? v[i] : 0.f;
+        } else {
           uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) + row + c0);
           if (!valid) w = make_uint4(0, 0, 0, 0);
-          xh[sp][ks] = __builtin_bit_cast(bf16x8, w);
-        } else {
-          float v[8];
-          load8<F32IO>(xin, row + c0, v);
+          if constexpr (kKeepRow) {
+            raw[s][4 * ks + 0] = w.x;
+            raw[s][4 * ks + 1] = w.y;
+            raw[s][4 * ks + 2] = w.z;
+            raw[s][4 * ks + 3] = w.w;
+          }
+          v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+          v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+          // bf16 Values: the loaded words are the MFMA operand (x = v exactly)
+          if constexpr (!kLo) xh[sp][ks] = __builtin_bit_cast(bf16x8, w);
+        }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float xf = valid ? (KEY ? s_lds[c0 + i] * v[i] : v[i]) : 0.f;
+        for (int i = 0; i < 8; ++i) {
+          const float xf = KEY ? s_lds[c0 + i] * v[i] : v[i];
+          q = fmaf(xf, v[i], q);
+          if constexpr (kLo) {
             const __bf16 hb = (__bf16)xf;
             xh[sp][ks][i] = hb;
             xl[sp][ks][i] = (__bf16)(xf - (float)hb);
           }
         }
       }
+      // pinned here, so the unpacked row is not kept alive to form it later
+      asm volatile("" : "+v"(q));
+      ksq[s] = q;
 #pragma unroll
       for (int i = 0; i < L; ++i) lst[s][i] = -INFINITY;
     }
 
-    for (int blk = 0; blk < Cpad / 32; ++blk) {
-      f32x16 acc[SPP];
+    // accumulators of centre block blk: start values, then the MFMA chain.
+    // Lane (token l32, half) holds centres blk*32 + 8(i/4) + 4*half + i%4.
+    auto mfma_blk = [&](int blk, f32x16 (&acc)[SPP]) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = init[blk * 32 + 8 * (i / 4) + 4 * half + (i % 4)];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(init + blk * 32 + 8 * q4 + 4 * half);
 #pragma unroll
-        for (int sp = 0; sp < SPP; ++sp) acc[sp][i] = v;
+        for (int sp = 0; sp < SPP; ++sp) {
+          acc[sp][4 * q4 + 0] = v4.x;
+          acc[sp][4 * q4 + 1] = v4.y;
+          acc[sp][4 * q4 + 2] = v4.z;
+          acc[sp][4 * q4 + 3] = v4.w;
+        }
       }
       const __bf16* arow = mu_hi + (blk * 32 + l32) * ROW + 8 * half;
 #pragma unroll
@@ -227,26 +271,91 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
             acc[sp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, xh[sp][ks], acc[sp], 0, 0, 0);
         }
       }
+    };
+    // keys of block blk: the score with its low pb bits replaced by the centre
+    // index; the lane-half bit (4 * half) is added after the screen, so the
+    // index here is wave-uniform
+    auto topl_blk = [&](int blk, const f32x16 (&acc)[SPP]) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t c = (uint32_t)(blk * 32 + 8 * (i / 4) + 4 * half + (i % 4));
+        uint32_t c = (uint32_t)(blk * 32 + 8 * (i / 4) + (i % 4));
+        asm volatile("" : "+s"(c));  // one scalar operand: the key is one v_and_or_b32
 #pragma unroll
-        for (int sp = 0; sp < SPP; ++sp) {
-          const float key = __uint_as_float((__float_as_uint(acc[sp][i]) & ~mask) | c);
-          topl_insert<L>(lst[pass * SPP + sp], key);
-        }
+        for (int sp = 0; sp < SPP; ++sp)
+          topl_insert<L>(lst[pass * SPP + sp], __uint_as_float((__float_as_uint(acc[sp][i]) & keep) | c));
       }
+    };
+    // issue order of one half step: the start values and first A fragment,
+    // then each MFMA followed by its share of the insertions and the next
+    // fragment read, so the matrix core and the VALU work side by side
+    constexpr int NMF = NG * SPP * (kLo ? 2 : 1) + (F32IO ? NG * SPP : 0);  // MFMAs per block
+    constexpr int NVA = 16 * SPP * (L + 1);                                  // key VALU per block
+    auto interleave = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (NVA + NMF - 1) / NMF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    f32x16 acc0[SPP], acc1[SPP];
+    mfma_blk(0, acc0);
+    int blk = 0;
+    for (; blk + 2 < nblk; blk += 2) {
+      mfma_blk(blk + 1, acc1);
+      topl_blk(blk, acc0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_blk(blk + 2, acc0);
+      topl_blk(blk + 1, acc1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
     }
+    mfma_blk(blk + 1, acc1);
+    topl_blk(blk, acc0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    topl_blk(blk + 1, acc1);
   }
 
-  // merge the two half-lists of each token (lanes t and t^32)
+  // the lane-half bit of the centre index joins the keys (-inf entries stay)
+  const uint32_t hbit = (uint32_t)half << 2;
 #pragma unroll
-  for (int s = 0; s < kSegsPerWave; ++s) {
+  for (int s = 0; s < kSegsPerWave; ++s)
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const float k = lst[s][i];
+      lst[s][i] = k > -INFINITY ? __uint_as_float(__float_as_uint(k) | hbit) : k;
+    }
+
+  // Lane = token from here: lane t takes token t of segment 0, lane t + 32
+  // token t of segment 1.  One v_permlane32_swap per register moves the upper
+  // half's segment-0 data down and the lower half's segment-1 data up, so each
+  // lane ends with both halves (lists, ||k||^2 parts, row words) of its token.
+  auto swap32 = [](uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  };
+  float mylst[L];
+  {
     float other[L];
 #pragma unroll
-    for (int i = 0; i < L; ++i) other[i] = __shfl_xor(lst[s][i], 32);
+    for (int i = 0; i < L; ++i) {
+      uint32_t a = __float_as_uint(lst[0][i]), b = __float_as_uint(lst[1][i]);
+      swap32(a, b);
+      mylst[i] = __uint_as_float(a);
+      other[i] = __uint_as_float(b);
+    }
 #pragma unroll
-    for (int i = 0; i < L; ++i) topl_insert<L>(lst[s], other[i]);
+    for (int i = 0; i < L; ++i) topl_insert<L>(mylst, other[i]);
+  }
+  float myksq;
+  {
+    uint32_t a = __float_as_uint(ksq[0]), b = __float_as_uint(ksq[1]);
+    swap32(a, b);
+    myksq = __uint_as_float(a) + __uint_as_float(b);
   }
 
   // ---- 2. certification ----
@@ -263,15 +372,6 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   const float mx = p.head_max[h * 4 + p.head_max_slot];
   const int kc = p.Kc;
   const int sidx = half;  // lane = token from here: segment `half`, token l32
-  float mylst[L];
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    // both lists pinned in registers first, so the per-lane choice is a
-    // select and not an indexed stack array
-    float a = lst[0][i], b = lst[1][i];
-    asm volatile("" : "+v"(a), "+v"(b));
-    mylst[i] = sidx ? b : a;
-  }
   const int mylen = sidx ? seg_len[1] : seg_len[0];
   const bool valid = l32 < mylen;
   const int first = sidx ? seg_first[1] : seg_first[0];
@@ -279,25 +379,38 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   const int frame = p.frame0 + (sidx ? seg_frame[1] : seg_frame[0]);
   const int tok_rel = first + (valid ? l32 : 0);
   const int64_t tok = p.tok0 + tok_rel;
-  const int64_t krow = (int64_t)tok_rel * p.token_stride;
-  // the token's row, loaded once into registers (packed bf16 pairs, or fp32);
-  // invalid lanes hold a clamped real row and are masked at every reduction
-  // and store
+  // The token's row in registers: bf16 Values take the screen's half rows
+  // (zero on invalid lanes); other rows are loaded again (invalid lanes hold a
+  // clamped real row).  Invalid lanes are masked at every reduction and store.
   uint32_t kw[F32IO ? D : D / 2];
+  if constexpr (F32IO) {
+    const int64_t krow = (int64_t)tok_rel * p.token_stride;
 #pragma unroll
-  for (int j8 = 0; j8 < NV; ++j8) {
-    if constexpr (F32IO) {
+    for (int j8 = 0; j8 < NV; ++j8) {
       float v[8];
       load8<true>(xin, krow + 8 * j8, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) kw[8 * j8 + i] = __float_as_uint(v[i]);
-    } else {
+    }
+  } else if constexpr (!kKeepRow) {
+    const int64_t krow = (int64_t)tok_rel * p.token_stride;
+#pragma unroll
+    for (int j8 = 0; j8 < NV; ++j8) {
       const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) + krow + 8 * j8);
       kw[4 * j8 + 0] = w.x;
       kw[4 * j8 + 1] = w.y;
       kw[4 * j8 + 2] = w.z;
       kw[4 * j8 + 3] = w.w;
     }
+  } else {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        swap32(raw[0][4 * g + i], raw[1][4 * g + i]);
+        kw[8 * g + i] = raw[0][4 * g + i];      // channels 16g + 2i, 16g + 2i + 1
+        kw[8 * g + 4 + i] = raw[1][4 * g + i];  // channels 16g + 8 + 2i, ...
+      }
   }
   // Register fence on the packed row: an empty asm that the compiler must
   // assume rewrites the words, so unpacked copies are not kept alive across
@@ -306,14 +419,6 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
 #pragma unroll
     for (int i = 0; i < (F32IO ? D : D / 2); ++i) asm volatile("" : "+v"(kw[i]));
   };
-  auto kval = [&](int j) -> float {
-    if constexpr (F32IO) return __uint_as_float(kw[j]);
-    else return (j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1]);
-  };
-  // ||k||_s^2 of this lane's token (only used inside the error bound)
-  float myksq = 0.f;
-#pragma unroll
-  for (int j = 0; j < D; ++j) myksq = fmaf(s_lds[j] * kval(j), kval(j), myksq);
   // Bars of every tracked entry from its own centre's norm (the nearest centres
   // are typically far from the largest norm); the untracked centres, whose keys
   // are at most the last tracked key, are bounded with the head's largest norm
@@ -611,37 +716,40 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   int chosen = cand[0];
   if constexpr (KEY && KC > 1) {
     if (p.use_range) {
+      // P_c = sum_g S_g range_g(k - mu_c)^2 for every tracked candidate at once:
+      // each residual group of the row is unpacked once for all K_c centres
       const double* sg = p.sgroup + (int64_t)h * NG;
+      double P[KC];
+#pragma unroll
+      for (int i = 0; i < KC; ++i) P[i] = 0.0;
+#pragma unroll 1
+      for (int g = 0; g < NG; ++g) {
+        float k[16];
+        load_k16(g, k);
+        const double sgv = p.uniform ? 16.0 : sg[g];
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+          float m[16];
+          mu_row16(cand[i], g, m);
+          float lo = k[0] - m[0], hi = lo;
+#pragma unroll
+          for (int j = 1; j < 16; ++j) {
+            const float rho = k[j] - m[j];
+            lo = fminf(lo, rho);
+            hi = fmaxf(hi, rho);
+          }
+          const double rg = (double)hi - (double)lo;
+          P[i] = fma(sgv, rg * rg, P[i]);
+        }
+      }
       double bestP = INFINITY;
       float bestD = INFINITY;
       int best = 0x7fffffff;
-#pragma unroll 1
-      for (int i = 0; i < kc; ++i) {
-        int c = cand[0];
-        float td = tieD[0];
 #pragma unroll
-        for (int q = 1; q < KC; ++q)
-          if (q == i) { c = cand[q]; td = tieD[q]; }
-        if (c < C) {  // c >= C: padding rows when C < K_c
-          double P = 0.0;
-#pragma unroll 1
-          for (int g = 0; g < NG; ++g) {
-            float k[16], m[16];
-            load_k16(g, k);
-            mu_row16(c, g, m);
-            float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const float rho = k[j] - m[j];
-              lo = fmin_fast(lo, rho);
-              hi = fmax_fast(hi, rho);
-            }
-            const double rg = (double)hi - (double)lo;
-            P = fma(p.uniform ? 16.0 : sg[g], rg * rg, P);
-          }
-          const bool better = (P < bestP) || (P == bestP && (td < bestD || (td == bestD && c < best)));
-          if (better) { bestP = P; bestD = td; best = c; }
-        }
+      for (int i = 0; i < KC; ++i) {
+        const int c = cand[i];
+        const bool better = (P[i] < bestP) || (P[i] == bestP && (tieD[i] < bestD || (tieD[i] == bestD && c < best)));
+        if (i < kc && c < C && better) { bestP = P[i]; bestD = tieD[i]; best = c; }
       }
       chosen = best < C ? best : cand[0];  // all-NaN scores keep a valid index
     }
@@ -663,33 +771,39 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
     load_k16(g, k);
     mu_row16(chosen, g, m);
     float rho[16];
-    float lo = INFINITY, hi = -INFINITY;
+    rho[0] = k[0] - m[0];
+    float lo = rho[0], hi = rho[0];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 1; j < 16; ++j) {
       rho[j] = k[j] - m[j];
-      lo = fmin_fast(lo, rho[j]);
-      hi = fmax_fast(hi, rho[j]);
+      lo = fminf(lo, rho[j]);
+      hi = fmaxf(hi, rho[j]);
     }
     if (!valid) { lo = INFINITY; hi = -INFINITY; }
-    for (int off = 1; off < T; off <<= 1) {
-      lo = fmin_fast(lo, __shfl_xor(lo, off));
-      hi = fmax_fast(hi, __shfl_xor(hi, off));
-    }
+    // min / max over the T lanes of the tile (T | 32, tiles lane-aligned)
+    if (T > 1) { lo = fminf(lo, dpp_f<0xB1>(lo)); hi = fmaxf(hi, dpp_f<0xB1>(hi)); }    // lane ^ 1
+    if (T > 2) { lo = fminf(lo, dpp_f<0x4E>(lo)); hi = fmaxf(hi, dpp_f<0x4E>(hi)); }    // lane ^ 2
+    if (T > 4) { lo = fminf(lo, dpp_f<0x141>(lo)); hi = fmaxf(hi, dpp_f<0x141>(hi)); }  // 7 - lane in 8
+    if (T > 8) { lo = fminf(lo, dpp_f<0x140>(lo)); hi = fmaxf(hi, dpp_f<0x140>(hi)); }  // 15 - lane in 16
+    if (T > 16) { lo = fminf(lo, __shfl_xor(lo, 16)); hi = fmaxf(hi, __shfl_xor(hi, 16)); }
     const uint16_t zb = to_half_bits(lo);
     const uint16_t sb = to_half_bits((hi - lo) / 3.0f);
     const float zf = half_bits_to_float(zb);
     const float sf = half_bits_to_float(sb);
-    const float t1 = zf + 0.5f * sf, t2 = zf + 1.5f * sf, t3 = zf + 2.5f * sf;
+    // a zero scale codes everything as 0 (every finite residual is below +inf)
+    const bool zs = sf == 0.f;
+    const float t1 = zs ? INFINITY : zf + 0.5f * sf;
+    const float t2 = zs ? INFINITY : zf + 1.5f * sf;
+    const float t3 = zs ? INFINITY : zf + 2.5f * sf;
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      uint32_t code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
-      code = sf != 0.f ? code : 0u;  // a zero scale codes everything as 0
+      const uint32_t code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
       w |= code << (2 * j);
       if constexpr (KEY && R > 0) {
         const float rhat = fmaf((float)code, sf, zf);
         const double e = ((double)k[j] - (double)m[j]) - (double)rhat;
-        const double* urow = U + (int64_t)(16 * g + j) * p.rp;
+        const double* urow = U + (16 * g + j) * R;
 #pragma unroll
         for (int i = 0; i < R; ++i) cacc[i] = fma(urow[i], e, cacc[i]);
         // one U row in flight at a time: the empty asm statements below (they

@@ -51,7 +51,7 @@ int check_config(const qwm_config* c) {
   if (cap > (int64_t)1 << 30) return QWM_ERR_UNSUPPORTED;
   // codebook + start values must fit in LDS (160 KiB per workgroup)
   const int cmax = std::max(c->num_centroids_k, c->num_centroids_v);
-  if (qwm::append_lds_bytes(ceil_div(cmax, 32) * 32, c->head_dim, c->io_dtype == QWM_F32, rpitch(c->rank), 8) >
+  if (qwm::append_lds_bytes(qwm::append_cpad(cmax), c->head_dim, c->io_dtype == QWM_F32, rpitch(c->rank), 8) >
       160 * 1024)
     return QWM_ERR_UNSUPPORTED;
   return QWM_OK;
@@ -588,7 +588,7 @@ int fill_append(const qwm_config* cfg, const qwm_cache* cache, const void* x, in
     p.codes = reinterpret_cast<uint32_t*>(cb + L.codes_v);
     p.params = reinterpret_cast<uint32_t*>(cb + L.params_v);
   }
-  p.Cpad = ceil_div(p.C, 32) * 32;
+  p.Cpad = qwm::append_cpad(p.C);
   p.sens = reinterpret_cast<const float*>(kb + L.sens);
   p.u64 = reinterpret_cast<const double*>(kb + L.u64);
   p.rp = rpitch(cfg->rank);

@@ -14,6 +14,8 @@ namespace qwm {
 // a segment.
 constexpr int kSegTokens = 32;
 constexpr int kSegsPerWave = 2;          // one 32-token MFMA N-block each
+// centre rows staged for the screen: C rounded up to whole pairs of 32-centre blocks
+inline int append_cpad(int C) { return (C + 63) / 64 * 64; }
 
 struct AppendParams {
   // input activations [H][n_new][d]
@@ -24,7 +26,7 @@ struct AppendParams {
   int F, T, tpf;       // frame tokens, group tokens, tiles per frame
   int segs_per_frame;  // ceil(F / 32)
   int total_segs;      // (n_new / F) * segs_per_frame
-  int C, Cpad;         // centres (padded to a multiple of 32)
+  int C, Cpad;         // centres (padded to a multiple of 64: an even number of 32-centre blocks)
   int Kc;              // tracked candidates: K_c for QSAC, 1 for argmin modes
   int use_range;       // QSAC stage 2 active
   int uniform;         // s = 1
