@@ -16,8 +16,8 @@
 //     argmax F = argmin D.  A = 32 centres x 16 channels from LDS, B = 32
 //     tokens x 16 channels from registers; the accumulator starts at
 //     -||mu||_s^2/2.  Lane (t, h) ends with token t's scores of 16 centres per
-//     block; it keeps the top K_c + 2 as float keys whose low bits carry the
-//     centre index (one bit-select, K_c + 1 med3 and one max per score).  The
+//     block; it keeps the top K_c + 3 (Values: 3) as float keys whose low bits
+//     carry the centre index (one and-or, L - 1 med3 and one max per score).  The
 //     MFMAs of the next block run while the keys of this one are inserted.
 //  2. Lane = token: v_permlane32_swap hands lane t token t of the first segment
 //     and lane t + 32 token t of the second, with both halves of its list and
@@ -94,7 +94,10 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NG = D / 16;      // residual groups (= MFMA k-steps of 16 channels)
   constexpr int ROW = D + kPad;   // LDS row pitch (bf16 elements)
-  constexpr int L = KC + 2;       // tracked keys: K_c, the next one and one spare for rescoring
+  // tracked keys: K_c, the next one and spares for rescoring (two for Keys,
+  // whose lists otherwise fall back to the all-centre search for about one
+  // token in 3000; one for Values)
+  constexpr int L = KEY ? KC + 3 : KC + 2;
   constexpr int NV = D / 8;       // 8-value chunks per row
 
   const int h = blockIdx.y;
@@ -116,10 +119,13 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   const void* mu_g = F32IO ? static_cast<const void*>(static_cast<const float*>(p.mu) + (int64_t)h * C * D)
                            : static_cast<const void*>(static_cast<const uint16_t*>(p.mu) + (int64_t)h * C * D);
 
-  // ---- stage the codebook, the accumulator start values and s in LDS ----
-  for (int e = threadIdx.x; e < Cpad * NV; e += NTH) {
-    const int c = e / NV, j8 = (e % NV) * 8;
-    if constexpr (F32IO) {
+  // ---- stage the codebook, the accumulator start values, s and U in LDS ----
+  // bf16 codebooks: every global load of a thread is issued before its LDS
+  // stores, so staging costs about one memory latency (16 row chunks per
+  // thread cover every supported C in one round)
+  if constexpr (F32IO) {
+    for (int e = threadIdx.x; e < Cpad * NV; e += NTH) {
+      const int c = e / NV, j8 = (e % NV) * 8;
       float v[8];
       if (c < C) load8<true>(mu_g, (int64_t)c * D + j8, v);
       else for (int i = 0; i < 8; ++i) v[i] = 0.f;
@@ -130,20 +136,59 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
       }
       *reinterpret_cast<bf16x8*>(mu_hi + c * ROW + j8) = hi;
       *reinterpret_cast<bf16x8*>(mu_lo + c * ROW + j8) = lo;
-    } else {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (c < C) w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(mu_g) + (int64_t)c * D + j8);
-      *reinterpret_cast<uint4*>(mu_hi + c * ROW + j8) = w;
+    }
+  } else {
+    constexpr int CH = 16;
+    const int total = Cpad * NV;
+    for (int base = 0; base < total; base += CH * NTH) {
+      uint4 w[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int e = min(base + u * NTH + (int)threadIdx.x, total - 1);
+        const int c = e / NV, j8 = (e % NV) * 8;
+        w[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(mu_g) + (int64_t)min(c, C - 1) * D + j8);
+        if (c >= C) w[u] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int e = base + u * NTH + (int)threadIdx.x;
+        if (e < total) *reinterpret_cast<uint4*>(mu_hi + (e / NV) * ROW + (e % NV) * 8) = w[u];
+      }
     }
   }
-  for (int c = threadIdx.x; c < Cpad; c += NTH)
-    init[c] = c < C ? -p.norm_half[(int64_t)h * C + c] : -3.0e38f;
-  for (int j = threadIdx.x; j < D; j += NTH) {
-    const float sj = p.uniform ? 1.f : p.sens[(int64_t)h * D + j];
-    s_lds[j] = sj;
+  {
+    constexpr int IPT = (512 + NTH - 1) / NTH;                   // start values per thread (C <= 512)
+    constexpr int UPT = (D * (R > 0 ? R : 1) + NTH - 1) / NTH;  // U entries per thread
+    float iv[IPT];
+    double uv[UPT];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int c = u * NTH + (int)threadIdx.x;
+      iv[u] = c < C ? -p.norm_half[(int64_t)h * C + c] : -3.0e38f;
+    }
+    const int jt = min((int)threadIdx.x, D - 1);
+    const float sj = p.uniform ? 1.f : p.sens[(int64_t)h * D + jt];
+    if constexpr (KEY && R > 0) {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int e = u * NTH + (int)threadIdx.x;
+        uv[u] = e < D * R ? p.u64[(int64_t)h * D * R + e] : 0.0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int c = u * NTH + (int)threadIdx.x;
+      if (c < Cpad) init[c] = iv[u];
+    }
+    if ((int)threadIdx.x < D) s_lds[threadIdx.x] = sj;
+    if constexpr (KEY && R > 0) {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int e = u * NTH + (int)threadIdx.x;
+        if (e < D * R) u_lds[e] = uv[u];
+      }
+    }
   }
-  if constexpr (KEY && R > 0)
-    for (int e = threadIdx.x; e < D * p.rp; e += NTH) u_lds[e] = p.u64[(int64_t)h * D * p.rp + e];
   __syncthreads();
 
   // ---- segments of this wave ----
@@ -800,17 +845,30 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
     for (int j = 0; j < 16; ++j) {
       const uint32_t code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
       w |= code << (2 * j);
-      if constexpr (KEY && R > 0) {
-        const float rhat = fmaf((float)code, sf, zf);
+    }
+    if constexpr (KEY && R > 0) {
+      // c += U^T e over the group's 16 channels, with the next U row read
+      // while this row's FMAs run: the empty asm statements (no instruction)
+      // keep the rows in order, so at most two rows are live
+      const double* ug = U + 16 * g * R;
+      double ucur[R], unxt[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) ucur[i] = ug[i];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j + 1 < 16) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) unxt[i] = ug[(j + 1) * R + i];
+        }
+        const float rhat = fmaf((float)((w >> (2 * j)) & 3u), sf, zf);
         const double e = ((double)k[j] - (double)m[j]) - (double)rhat;
-        const double* urow = U + (16 * g + j) * R;
 #pragma unroll
-        for (int i = 0; i < R; ++i) cacc[i] = fma(urow[i], e, cacc[i]);
-        // one U row in flight at a time: the empty asm statements below (they
-        // emit no instruction) pin this row's FMAs before the next row's LDS
-        // reads, so the rows are not all loaded up front
+        for (int i = 0; i < R; ++i) cacc[i] = fma(ucur[i], e, cacc[i]);
 #pragma unroll
-        for (int i = 0; i < R; ++i) asm volatile("" : "+v"(cacc[i]));
+        for (int i = 0; i < R; ++i) {
+          asm volatile("" : "+v"(cacc[i]));
+          ucur[i] = unxt[i];
+        }
         asm volatile("" ::: "memory");
       }
     }
