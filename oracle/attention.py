@@ -21,10 +21,20 @@ Readings: softmax scale 1/sqrt(d); inputs are the post-positional-encoding
 Q/K that enter the dot product; the current chunk's own K/V are not part of
 the compressed cache (lse is returned so a caller can merge them).
 
+One generation step (attention_with_local): the chunk's queries attend to the
+rebuilt cache and to the chunk's own uncompressed keys and values (the pages
+describe generation that reads the growing cache of historical frames while
+the current frames are produced: digest, opening paragraph).  Reading: every
+key of the chunk is visible to every query of the chunk (the chunk is one
+block; no mask inside it).
+
 Pins (tests/test_oracle_attention.py): zero-residual keys reduce to textbook
 softmax attention (PyTorch CPU scaled_dot_product_attention in float64);
 constant V gives o = v; softmax rows sum to one; a split-KV log-sum-exp merge
 equals the unsplit result; brute-force per-query loops on the tiny case.
+attention_with_local: brute-force loops over both key sets; an empty cache
+gives PyTorch's scaled_dot_product_attention over the local keys; local keys
+that repeat the cache's keys leave o unchanged and raise lse by log 2.
 """
 import numpy as np
 
@@ -87,3 +97,16 @@ def merge_partials(parts):
     lse = top + np.log(w.sum(axis=0))
     o = sum(np.exp(p[1] - lse)[:, None] * p[0] for p in parts)
     return o, lse
+
+
+def attention_with_local(q, keys, values, k_loc, v_loc, scale=None):
+    """o [n_q, d] and lse [n_q] (float64) of one softmax over the rebuilt cache
+    keys/values and the chunk's own keys/values, all visible.  No keys at all
+    gives o = 0 and lse = -inf."""
+    q = np.asarray(q, np.float64)
+    d = q.shape[1]
+    k = np.concatenate([np.asarray(keys, np.float64).reshape(-1, d), np.asarray(k_loc, np.float64).reshape(-1, d)])
+    v = np.concatenate([np.asarray(values, np.float64).reshape(-1, d), np.asarray(v_loc, np.float64).reshape(-1, d)])
+    if k.shape[0] == 0:
+        return np.zeros_like(q), np.full(q.shape[0], -np.inf)
+    return softmax_attention(q, k, v, scale)

@@ -102,6 +102,49 @@ def test_bruteforce_attention_tiny(tiny):
         assert abs(m + math.log(tot) - lse[i]) < 1e-10
 
 
+def test_local_chunk_bruteforce():
+    """One softmax over cache and local keys, by per-query loops."""
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((3, 8))
+    kc, vc = rng.standard_normal((5, 8)), rng.standard_normal((5, 8))
+    kl, vl = rng.standard_normal((4, 8)), rng.standard_normal((4, 8))
+    o, lse = oa.attention_with_local(q, kc, vc, kl, vl)
+    for i in range(3):
+        keys = list(kc) + list(kl)
+        vals = list(vc) + list(vl)
+        ls = [sum(q[i, j] * kk[j] for j in range(8)) / math.sqrt(8) for kk in keys]
+        m = max(ls)
+        ws = [math.exp(x - m) for x in ls]
+        tot = sum(ws)
+        for j in range(8):
+            ref = sum(wt * vv[j] for wt, vv in zip(ws, vals)) / tot
+            assert abs(o[i, j] - ref) < 1e-12
+        assert abs(lse[i] - (m + math.log(tot))) < 1e-12
+
+
+def test_local_chunk_without_cache_is_sdpa():
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((6, 16))
+    kl, vl = rng.standard_normal((9, 16)), rng.standard_normal((9, 16))
+    o, _ = oa.attention_with_local(q, np.zeros((0, 16)), np.zeros((0, 16)), kl, vl)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kl)[None], torch.from_numpy(vl)[None])[0].numpy()
+    assert np.max(np.abs(o - ref)) < 1e-12
+    o0, l0 = oa.attention_with_local(q, np.zeros((0, 16)), np.zeros((0, 16)), np.zeros((0, 16)), np.zeros((0, 16)))
+    assert np.all(o0 == 0) and np.all(l0 == -np.inf)
+
+
+def test_local_chunk_repeating_the_cache():
+    """Every key twice: the same weights, so o is unchanged and lse gains log 2."""
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((4, 16))
+    k, v = rng.standard_normal((7, 16)), rng.standard_normal((7, 16))
+    o1, l1 = oa.attention_with_local(q, k, v, np.zeros((0, 16)), np.zeros((0, 16)))
+    o2, l2 = oa.attention_with_local(q, k, v, k, v)
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs(l2 - l1 - math.log(2.0))) < 1e-12
+
+
 def test_reconstruction_uses_frame_tiles():
     """Token t of a 1560-token frame uses tile (t // 1560) * 98 + (t % 1560) // 16."""
     assert oa.tile_index(1559, 1560, 16) == 97
