@@ -221,6 +221,25 @@ def main():
                     "traffic": traffic_from_profiles("attention", args.config, src_hash),
                     "algorithmic_flops_per_launch": flops, "ms_per_launch": round(attk_avg, 4)}
 
+    # one generation step's attention with the chunk's own keys and values:
+    # the query chunk over the full compressed cache and the next frame in
+    # bf16 (timed apart from the step, whole call including the merge)
+    F = w.frame_tokens
+    kl = dev(np.stack([workloads.kv_frames(w, h, "k", w.frames, w.frames + 1) for h in range(w.heads)]))
+    vl = dev(np.stack([workloads.kv_frames(w, h, "v", w.frames, w.frames + 1) for h in range(w.heads)]))
+    ws_l = torch.empty(max(qwm.workspace_bytes(cfg, w.n_tokens + F, w.n_q), 1), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        qwm.attention_local(cache, q, kl, vl, out=out, lse=lse, workspace=ws_l)
+    el = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    torch.cuda.synchronize()
+    for e in el:
+        e[0].record()
+        qwm.attention_local(cache, q, kl, vl, out=out, lse=lse, workspace=ws_l)
+        e[1].record()
+    torch.cuda.synchronize()
+    loc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in el]))
+    loc_tf = attn_flops(w, w.n_q, w.n_tokens + F) / (loc_ms * 1e-3) / 1e12
+
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
         "metric": METRIC,
@@ -250,6 +269,9 @@ def main():
                       "frac_mfma": round(achieved_tf / PEAK_FP16_TFLOPS, 4),
                       "flops_per_launch": flops,
                       "compressed_cache_gbs": round(stored / (attk_avg * 1e-3) / 1e9, 2)},
+        "attention_local": {"ms": round(loc_ms, 4), "local_tokens": F, "tflops": round(loc_tf, 2),
+                            "frac_mfma": round(loc_tf / PEAK_FP16_TFLOPS, 4),
+                            "flops_per_call": attn_flops(w, w.n_q, w.n_tokens + F)},
         "roofline": roofline,
         "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4),
                         "stored_bytes": stored, "original_bytes": original},
@@ -299,6 +321,25 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
     attk = np.array([e[3].elapsed_time(e[4]) for e in ev])
     flops = np.array([attn_flops(w, w.n_q, (f + 1) * F) for f in range(w.frames)])
     tf = flops / (attk * 1e-3) / 1e12
+    # one generation step's attention with the chunk's own keys and values:
+    # the query chunk over the full compressed cache and the next frame in
+    # bf16 (timed apart from the step, whole call including the merge)
+    F = w.frame_tokens
+    kl = dev(np.stack([workloads.kv_frames(w, h, "k", w.frames, w.frames + 1) for h in range(w.heads)]))
+    vl = dev(np.stack([workloads.kv_frames(w, h, "v", w.frames, w.frames + 1) for h in range(w.heads)]))
+    ws_l = torch.empty(max(qwm.workspace_bytes(cfg, w.n_tokens + F, w.n_q), 1), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        qwm.attention_local(cache, q, kl, vl, out=out, lse=lse, workspace=ws_l)
+    el = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    torch.cuda.synchronize()
+    for e in el:
+        e[0].record()
+        qwm.attention_local(cache, q, kl, vl, out=out, lse=lse, workspace=ws_l)
+        e[1].record()
+    torch.cuda.synchronize()
+    loc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in el]))
+    loc_tf = attn_flops(w, w.n_q, w.n_tokens + F) / (loc_ms * 1e-3) / 1e12
+
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
         "metric": METRIC, "value": round(w.n_tokens / wall / 1e3, 3), "unit": "Ktokens/s", "n_gpus": 1,

@@ -283,6 +283,31 @@ int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, const voi
                         float* lse, void* workspace, size_t ws_bytes, void* stream,
                         void* ev_kernel_begin, void* ev_kernel_end);
 
+/*
+ * One generation step's attention: the query chunk attends to the compressed
+ * cache and to the chunk's own uncompressed Keys and Values k_loc, v_loc
+ * [H][n_loc][d] (bf16; strides st_k, st_v), all of them visible to every query
+ * of the chunk.  The pages describe generation that reads the cached history
+ * while the current frames are produced ([digest], opening paragraph: the
+ * cache of historical frames grows as generation proceeds); the result is one
+ * softmax over both key sets:
+ *   out = sum_t softmax(l)_t w_t over t in (cache, local),
+ *   l_t = scale q.k~_t (cache) or scale q.k_t (local), w_t = v~_t or v_t,
+ *   lse = log sum_t exp(l_t).
+ * It equals the log-sum-exp merge of qwm_attention over the cache with plain
+ * softmax attention over the local keys.  Local rows enter the fp16
+ * contraction like the queries (exact for |x| in [2^-17, 65504]).  bf16
+ * activations only (fp32: QWM_ERR_UNSUPPORTED); n_loc = 0 is qwm_attention;
+ * n_k = 0 (empty cache) is attention over the local chunk alone.  Workspace:
+ * qwm_attention_workspace_size(cfg, n_k + n_loc, n_q).  Errors as for
+ * qwm_attention, plus QWM_ERR_INVALID_ARG for misaligned local rows.
+ */
+int qwm_attention_local(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                        const qwm_strides* st_q, const void* k_loc, const void* v_loc, int64_t n_loc,
+                        const qwm_strides* st_k, const qwm_strides* st_v, float scale, void* out,
+                        const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes,
+                        void* stream);
+
 /* The logits l [H][n_q][n_k] fp32 of the same kernel (debug variant), for
  * logit parity checks on small shapes. */
 int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, const void* q,

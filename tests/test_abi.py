@@ -116,6 +116,26 @@ def test_append_error_paths_move_no_counter():
     out_st = qwm.QwmStrides(880 * 128, 128)
     assert L.qwm_attention(ctypes.byref(c), ctypes.byref(h), _fake(), 880, ctypes.byref(st), ctypes.c_float(0),
                            _fake(0x300000), ctypes.byref(out_st), None, None, 0, None) == qwm.ERR_STATE
+    # attention with the local chunk: the same state check, then the local rows
+    assert L.qwm_attention_local(ctypes.byref(c), ctypes.byref(h), _fake(), 880, ctypes.byref(st), _fake(), _fake(),
+                                 880, ctypes.byref(st), ctypes.byref(st), ctypes.c_float(0), _fake(0x300000),
+                                 ctypes.byref(out_st), None, None, 0, None) == qwm.ERR_STATE
+    h.n_k = 0
+    assert L.qwm_attention_local(ctypes.byref(c), ctypes.byref(h), _fake(), 880, ctypes.byref(st), _fake(),
+                                 _fake(0x100002), 880, ctypes.byref(st), ctypes.byref(st), ctypes.c_float(0),
+                                 _fake(0x300000), ctypes.byref(out_st), None, None, 0, None) == qwm.ERR_INVALID_ARG
+    assert L.qwm_attention_local(ctypes.byref(c), ctypes.byref(h), _fake(), 880, ctypes.byref(st), _fake(), _fake(),
+                                 -1, ctypes.byref(st), ctypes.byref(st), ctypes.c_float(0), _fake(0x300000),
+                                 ctypes.byref(out_st), None, None, 0, None) == qwm.ERR_INVALID_ARG
+    # fp32 activations have no local-chunk path
+    wt = workloads.WORKLOADS["tiny"]
+    ct = cfg_of(wt).c()
+    ht = qwm.QwmCache()
+    assert L.qwm_cache_init(ctypes.byref(ct), _fake(), _fake(0x200000), ctypes.byref(ht)) == 0
+    stt = qwm.QwmStrides(wt.n_tokens * 64, 64)
+    assert L.qwm_attention_local(ctypes.byref(ct), ctypes.byref(ht), _fake(), 32, ctypes.byref(stt), _fake(), _fake(),
+                                 64, ctypes.byref(stt), ctypes.byref(stt), ctypes.c_float(0), _fake(0x300000),
+                                 ctypes.byref(stt), None, None, 0, None) == qwm.ERR_UNSUPPORTED
     # wrong abi version in the config
     c2 = cfg_of(w).c()
     c2.abi_version = 99

@@ -229,3 +229,82 @@ def test_full_size_480p_sampled():
         say("  head %d: attention max(|dO| - half ulp)/tol=%.3g max|dlse|/bound=%.3g" % (h, wo, wl))
         assert wo <= 1.0 and wl <= 1.0
     say("  append parity ok: %s" % dict(stats))
+
+
+def check_local(cfg, cal, outs, q, k_loc, v_loc, o, lse, heads):
+    """Attention over cache + local chunk against the oracle: worst output and
+    lse errors over their bounds (the bounds of check_attention, taken over
+    both key sets)."""
+    from oracle import attention as oa
+    worst_o, worst_l = 0.0, 0.0
+    for h in heads:
+        if outs is not None:
+            ko, vo = outs[h]
+            _, _, kr, vr = P.oracle_attention(cfg, cal, h, ko, vo, q[h][:1])
+        else:
+            kr = vr = np.zeros((0, cfg.head_dim))
+        kl, vl = k_loc[h].astype(np.float64), v_loc[h].astype(np.float64)
+        oo, ll = oa.attention_with_local(q[h], kr, vr, kl, vl)
+        vall = np.concatenate([vr, vl])
+        kall = np.concatenate([kr, kl])
+        tol = np.maximum(2e-2, 2.0 ** -11 * np.abs(vall).max(axis=0))[None, :]
+        worst_o = max(worst_o, float(np.max((np.abs(o[h] - oo) - P.bf16_half_ulp(oo)) / tol)))
+        ltol = 1e-3 / np.sqrt(cfg.head_dim) * np.linalg.norm(q[h].astype(np.float64), axis=1) * \
+            np.linalg.norm(kall, axis=1).max()
+        worst_l = max(worst_l, float(np.max(np.abs(lse[h] - ll) / ltol)))
+    return worst_o, worst_l
+
+
+@pytest.mark.parametrize("n_loc", [880, 100])
+def test_local_chunk_attention(n_loc):
+    """One generation step: the query chunk over the compressed cache (2
+    frames) and the chunk's own bf16 keys and values (the next frame, whole or
+    a ragged prefix), with stream-K pieces that straddle the two key sets."""
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=2)
+    cfg = P.cfg_of(w)
+    say("case local_chunk n_loc=%d" % n_loc)
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=3)
+    cache, _ = P.build_cache(cfg, cal, data["k"], data["v"])
+    gpu = P.gpu_fields(cache, cache.n_k)
+    stats = P.Stats()
+    outs = [(P.check_keys_head(cfg, data["k"][h], cal, h, gpu, stats),
+             P.check_values_head(cfg, data["v"][h], cal, h, gpu, stats)) for h in range(cfg.heads)]
+    k_loc = np.stack([workloads.kv_frames(w, h, "k", w.frames, w.frames + 1)[:n_loc] for h in range(cfg.heads)])
+    v_loc = np.stack([workloads.kv_frames(w, h, "v", w.frames, w.frames + 1)[:n_loc] for h in range(cfg.heads)])
+    q = P.to_dev(data["q"], cfg)
+    o, lse = qwm.attention_local(cache, q, P.to_dev(k_loc, cfg), P.to_dev(v_loc, cfg))
+    wo, wl = check_local(cfg, cal, outs, data["q"], k_loc, v_loc, o.float().cpu().numpy(), lse.cpu().numpy(),
+                         range(cfg.heads))
+    say("  local chunk: max(|dO| - half ulp)/tol=%.3g max|dlse|/bound=%.3g" % (wo, wl))
+    assert wo <= 1.0 and wl <= 1.0
+
+
+def test_local_chunk_edge_cases():
+    """Empty cache (local keys alone); no local keys (the cache-only kernel,
+    bit for bit); one ragged local tile over an empty cache."""
+    import torch
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=1)
+    cfg = P.cfg_of(w)
+    say("case local_chunk_edges")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    cache, calib = P.build_cache(cfg, cal, data["k"], data["v"])
+    q = P.to_dev(data["q"][:, :300], cfg)
+    k_loc = np.stack([workloads.kv_frames(w, h, "k", 1, 2) for h in range(cfg.heads)])
+    v_loc = np.stack([workloads.kv_frames(w, h, "v", 1, 2) for h in range(cfg.heads)])
+    kd, vd = P.to_dev(k_loc, cfg), P.to_dev(v_loc, cfg)
+    # no local keys: identical to qwm.attention
+    o_a, l_a = qwm.attention(cache, q)
+    o_b, l_b = qwm.attention_local(cache, q, kd[:, :0], vd[:, :0])
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+    # empty cache: attention over the local chunk alone
+    empty = qwm.Cache(cfg, calib)
+    for n in (880, 37):
+        o, lse = qwm.attention_local(empty, q, kd[:, :n].contiguous(), vd[:, :n].contiguous())
+        wo, wl = check_local(cfg, cal, None, data["q"][:, :300], k_loc[:, :n], v_loc[:, :n],
+                             o.float().cpu().numpy(), lse.cpu().numpy(), range(cfg.heads))
+        say("  empty cache, n_loc=%d: %.3g %.3g" % (n, wo, wl))
+        assert wo <= 1.0 and wl <= 1.0

@@ -23,8 +23,8 @@ UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE = 1, 2, 3
 
 EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint", "qwm_calibrate_host",
            "qwm_calib_import", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
-           "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention", "qwm_attention_timed",
-           "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
+           "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention",
+           "qwm_attention_timed", "qwm_attention_local", "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
 
 
 class QwmConfig(ctypes.Structure):
@@ -88,6 +88,8 @@ def lib():
                                              ctypes.c_size_t, P]),
             "qwm_attention_timed": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, ST, P, P,
                                                    ctypes.c_size_t, P, P, P]),
+            "qwm_attention_local": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P, I64, ST, ST, F,
+                                                   P, ST, P, P, ctypes.c_size_t, P]),
             "qwm_attention_logits": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, P]),
             "qwm_top1": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P]),
             "qwm_dense_top1": (ctypes.c_int, [CFG, P, I64, ST, P, I64, ST, P, P]),
@@ -316,6 +318,31 @@ def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float 
                                         ctypes.byref(sq), scale, _ptr(out), ctypes.byref(so), _ptr(lse),
                                         _ptr(workspace), nb, _stream(), ctypes.c_void_p(e0.cuda_event),
                                         ctypes.c_void_p(e1.cuda_event)))
+    return out, lse
+
+
+def attention_local(cache: Cache, q, k_loc, v_loc, out=None, lse=None, workspace=None, scale: float = 0.0):
+    """Attention of the query chunk q over the compressed cache and the chunk's
+    own uncompressed keys and values k_loc, v_loc [H][n_loc][d] (bf16)."""
+    torch = _torch()
+    cfg = cache.cfg
+    n_loc = k_loc.shape[1]
+    if v_loc.shape[1] != n_loc:
+        raise ValueError("k_loc and v_loc hold different token counts")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(cfg.heads, q.shape[1], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = workspace_bytes(cfg, cache.n_k + n_loc, q.shape[1])
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    c = cfg.c()
+    sq, sk, sv, so = strides(q), strides(k_loc), strides(v_loc), strides(out)
+    nb = workspace.numel() if workspace is not None else 0
+    check(lib().qwm_attention_local(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1],
+                                    ctypes.byref(sq), _ptr(k_loc), _ptr(v_loc), n_loc, ctypes.byref(sk),
+                                    ctypes.byref(sv), scale, _ptr(out), ctypes.byref(so), _ptr(lse),
+                                    _ptr(workspace), nb, _stream()))
     return out, lse
 
 

@@ -63,7 +63,8 @@ struct Grid {
   int n_qb;        // query blocks per head
   int qpb;         // queries per block: a multiple of 32, at most BM
   int heads;
-  int ntiles;      // key tiles of the cache
+  int ntiles;      // key tiles: the compressed cache's, then the local chunk's
+  int ntc;         // key tiles of the compressed cache (tiles >= ntc are local)
   long long units; // heads * n_qb * ntiles
   int G;           // workgroups with work
   int per_xcd;     // ceil(G / 8): workgroups w of one XCD take a contiguous run
@@ -131,7 +132,10 @@ __device__ __forceinline__ void rebuild16(uint32_t w, uint32_t zs, const uint4& 
 
 // One segment: pair (head, query block), key tiles [tb, te).  slot < 0: the
 // segment covers the pair's whole key range (final output), else partial.
-template <int D, bool PS, int NW>
+// LOCAL: the key axis continues with the local chunk's tiles.  Its tile
+// helpers (the *_t lambdas) are used by that instantiation only; the
+// cache-only kernel keeps the loop on key offsets.
+template <int D, bool PS, int NW, bool LOCAL>
 __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, _Float16* lds, int pair, int tb,
                                                int te, int slot) {
   constexpr int NT = 64 * NW;             // threads per workgroup
@@ -158,6 +162,12 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   const bool qvalid = wave_active && qi < p.n_q;
   const int kbeg = tb * BN;
   const int kend = min(p.n_k, te * BN);
+  // local-chunk kernel: tiles [0, ntc) hold the compressed cache, tiles
+  // [ntc, ntiles) the local bf16 keys and values (both from key 0 of their
+  // part); keys past a part's end are masked, prefetches past it read its
+  // last key again
+  auto t_local = [&](int t) { return t >= gr.ntc; };
+  auto t_key0 = [&](int t) { return (t >= gr.ntc ? t - gr.ntc : t) * BN; };
   const int ntiles = te - tb;
 
   // ---- Q fragment [q | U^T q] in fp16, paired channel order ----
@@ -267,6 +277,30 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       m1[u] = m[1];
     }
   };
+  // tile-indexed loads of the local-chunk kernel: cache fields for compressed
+  // tiles, the bf16 rows themselves (into m0, m1) for local ones
+  auto load_cache_t = [&](int t, Raw& r) {
+    t = min(t, gr.ntiles - 1);
+    if (!t_local(t)) load_cache(t * BN, r);
+  };
+  auto load_mu_t = [&](int t, const Raw& r) {
+    t = min(t, gr.ntiles - 1);
+    if (!t_local(t)) {
+      load_mu(r);
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int kk = min(t_key0(t) + it_key[u], p.n_loc - 1);
+      const uint16_t* row = it_v[u] ? static_cast<const uint16_t*>(p.v_loc) + (int64_t)h * p.vl_head_stride +
+                                          (int64_t)kk * p.vl_token_stride
+                                    : static_cast<const uint16_t*>(p.k_loc) + (int64_t)h * p.kl_head_stride +
+                                          (int64_t)kk * p.kl_token_stride;
+      const uint4* m = reinterpret_cast<const uint4*>(row + 16 * it_g[u]);
+      m0[u] = m[0];
+      m1[u] = m[1];
+    }
+  };
   const uint32_t magic_v = 0x64006400u;  // kept in a VGPR, the mask in an SGPR (one constant-bus read)
   const uint32_t mask_s = 0x00030003u;
   auto rebuild = [&](int buf, const Raw& r) {
@@ -289,6 +323,35 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     }
   };
 
+  // rebuild of tile t in the local-chunk kernel: local rows are converted
+  // from bf16 to fp16 in paired channel order, their PSAC columns are zero
+  auto rebuild_t = [&](int buf, const Raw& r, int t) {
+    if (!t_local(min(t, gr.ntiles - 1))) {
+      rebuild(buf, r);
+      return;
+    }
+    _Float16* base = lds + buf * BUF;
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const uint32_t a[4] = {m0[u].x, m0[u].y, m0[u].z, m0[u].w}, b[4] = {m1[u].x, m1[u].y, m1[u].z, m1[u].w};
+      uint32_t w[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const uint32_t x = a[jj >> 1], y = b[jj >> 1];
+        const float lo = __uint_as_float((jj & 1) ? (x & 0xffff0000u) : (x << 16));
+        const float hi = __uint_as_float((jj & 1) ? (y & 0xffff0000u) : (y << 16));
+        w[jj] = as_u32(h2_t{(_Float16)lo, (_Float16)hi});
+      }
+      _Float16* dst = it_v[u] ? base + KT + it_key[u] * VROW + 16 * it_g[u] : base + it_key[u] * KROW + 16 * it_g[u];
+      reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+    if constexpr (PS) {
+#pragma unroll
+      for (int v = 0; v < PPT; ++v) *reinterpret_cast<uint32_t*>(base + pk[v] * KROW + D + ppos[v]) = 0u;
+    }
+  };
+
   float m_run = -INFINITY;  // running max, log2 units
   float l_run = 0.f;        // this lane's share of the sum of probabilities
   f32x16 o[NDB];
@@ -298,10 +361,17 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
   if (ntiles > 0) {
-    load_cache(kbeg, ra);
-    load_mu(ra);
-    rebuild(0, ra);
-    load_cache(kbeg + BN, ra);
+    if constexpr (LOCAL) {
+      load_cache_t(tb, ra);
+      load_mu_t(tb, ra);
+      rebuild_t(0, ra, tb);
+      load_cache_t(tb + 1, ra);
+    } else {
+      load_cache(kbeg, ra);
+      load_mu(ra);
+      rebuild(0, ra);
+      load_cache(kbeg + BN, ra);
+    }
   }
   __syncthreads();
 
@@ -309,9 +379,16 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   const int trow = 4 * hf + ((lane & 15) >> 2);             // transposed read: key row in a 16-key chunk
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // and channel position in a 32-channel block
   for (int j = 0; j < ntiles; ++j) {
-    const int t0 = kbeg + j * BN;
-    load_mu(ra);                    // centre rows of tile j+1
-    load_cache(t0 + 2 * BN, rb);    // cache fields of tile j+2
+    const int t0 = LOCAL ? t_key0(tb + j) : kbeg + j * BN;
+    // end of the keys of this tile's part (local kernel), else of the segment
+    const int tend = LOCAL ? (t_local(tb + j) ? p.n_loc : p.n_k) : kend;
+    if constexpr (LOCAL) {
+      load_mu_t(tb + j + 1, ra);    // centre rows (local tiles: the rows) of tile j+1
+      load_cache_t(tb + j + 2, rb);
+    } else {
+      load_mu(ra);                  // centre rows of tile j+1
+      load_cache(t0 + 2 * BN, rb);  // cache fields of tile j+2
+    }
     const _Float16* kt = lds + (j & 1) * BUF;
     const _Float16* vt = kt + KT;
     if (__builtin_amdgcn_readfirstlane(wave_active)) {
@@ -334,12 +411,12 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (__builtin_amdgcn_readfirstlane(t0 + BN > kend)) {  // last tile only (uniform)
+      if (__builtin_amdgcn_readfirstlane(t0 + BN > tend)) {  // last tile of a part (uniform)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (t0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3) >= kend) s[mb][i] = -INFINITY;
+            if (t0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3) >= tend) s[mb][i] = -INFINITY;
       }
       // ---- online softmax, base 2 ----
       float mx = s[0][0];
@@ -373,7 +450,8 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
       // rebuild of the next tile into the other buffer: independent VALU work
       // for the scheduler to place among the P V MFMAs
-      rebuild((j + 1) & 1, ra);
+      if constexpr (LOCAL) rebuild_t((j + 1) & 1, ra, tb + j + 1);
+      else rebuild((j + 1) & 1, ra);
       // ---- O^T += V~^T P^T ----
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -386,7 +464,8 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
           o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
         }
     } else {
-      rebuild((j + 1) & 1, ra);
+      if constexpr (LOCAL) rebuild_t((j + 1) & 1, ra, tb + j + 1);
+      else rebuild((j + 1) & 1, ra);
     }
     ra = rb;
     __syncthreads();
@@ -429,15 +508,17 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   }
 }
 
-template <int D, bool PS, int NW>
+// LOCAL: the key axis continues with the local chunk's tiles (a separate
+// instantiation, so the cache-only kernel carries none of their code)
+template <int D, bool PS, int NW, bool LOCAL>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p, Grid gr) {
   constexpr int BUF = BN * (D + 24) + BN * (D + 32);
   __shared__ __align__(16) _Float16 lds[2 * BUF];
   const int bid = blockIdx.x;
   const int w = (bid & 7) * gr.per_xcd + (bid >> 3);
   if (w >= gr.G) return;
-  if (gr.ntiles == 0) {  // empty cache: every pair writes zeros and lse = -inf
-    attend_segment<D, PS, NW>(p, gr, lds, w, 0, 0, -1);
+  if (gr.ntiles == 0) {  // no keys at all: every pair writes zeros and lse = -inf
+    attend_segment<D, PS, NW, LOCAL>(p, gr, lds, w, 0, 0, -1);
     return;
   }
   const long long u0 = (long long)w * gr.units / gr.G;
@@ -449,7 +530,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p
     const int tb = (int)(u % gr.ntiles);
     const int te = (int)min<long long>(gr.ntiles, tb + (u1 - u));
     const int slot = (tb == 0 && te == gr.ntiles) ? -1 : (first ? 2 * w : 2 * w + 1);
-    attend_segment<D, PS, NW>(p, gr, lds, pair, tb, te, slot);
+    attend_segment<D, PS, NW, LOCAL>(p, gr, lds, pair, tb, te, slot);
     u += te - tb;
     first = false;
     __syncthreads();  // the next segment's first rebuild reuses buffer 0
@@ -514,7 +595,8 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
   g.n_qb = (p.n_q + BM - 1) / BM;
   const int per = (p.n_q + g.n_qb - 1) / g.n_qb;  // balance the query blocks
   g.qpb = (per + 31) / 32 * 32;
-  g.ntiles = (p.n_k + BN - 1) / BN;
+  g.ntc = (p.n_k + BN - 1) / BN;
+  g.ntiles = g.ntc + (p.n_loc + BN - 1) / BN;
   const long long pairs = (long long)g.n_qb * heads;
   g.units = pairs * g.ntiles;
   if (g.ntiles == 0 || !p.part_o) {
@@ -532,7 +614,10 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
     const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(p.ev_begin), stream);
     if (er != hipSuccess) return er;
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
+  if (p.n_loc > 0)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves, true>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves, false>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;

@@ -717,6 +717,20 @@ QWM_API size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tok
   return (size_t)splits * cfg->num_heads * n_q * ((size_t)cfg->head_dim * 4 + 4) + 256;
 }
 
+// bf16 activations: stream-K partials when the workspace holds them, else one
+// whole (head, query block) per workgroup
+int run_attention_bf16(const qwm_config* cfg, qwm::AttnParams& p, void* workspace, size_t ws_bytes, void* stream) {
+  if (p.n_k + p.n_loc > 0 && ws_bytes >= bf16_partial_bytes(cfg)) {
+    const size_t rows = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
+    p.part_o = static_cast<float*>(workspace);  // holds fp16 rows on this path
+    p.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                         align256(rows * (size_t)cfg->head_dim * 2));
+  }
+  hipError_t e = qwm::launch_attention(p, cfg->num_heads, cfg->head_dim, false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return QWM_OK;
+}
+
 QWM_API int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
                                 const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
                                 float* lse, void* workspace, size_t ws_bytes, void* stream, void* ev_kernel_begin,
@@ -734,19 +748,7 @@ QWM_API int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, c
   p.o_head_stride = st_out->head;
   p.o_token_stride = st_out->token;
   p.lse = lse;
-  if (cfg->io_dtype == QWM_BF16) {
-    // stream-K partials when the workspace holds them, else one whole
-    // (head, query block) per workgroup
-    if (p.n_k > 0 && ws_bytes >= bf16_partial_bytes(cfg)) {
-      const size_t rows = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
-      p.part_o = static_cast<float*>(workspace);  // holds fp16 rows on this path
-      p.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                           align256(rows * (size_t)cfg->head_dim * 2));
-    }
-    hipError_t e = qwm::launch_attention(p, cfg->num_heads, cfg->head_dim, false, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e);
-    return QWM_OK;
-  }
+  if (cfg->io_dtype == QWM_BF16) return run_attention_bf16(cfg, p, workspace, ws_bytes, stream);
   int splits = choose_splits(cfg, p.n_k, n_q);
   const size_t per_split = (size_t)cfg->num_heads * n_q * ((size_t)cfg->head_dim * 4 + 4);
   while (splits > 1 && (size_t)splits * per_split + 256 > ws_bytes) --splits;
@@ -764,6 +766,37 @@ QWM_API int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, c
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return QWM_OK;
+}
+
+QWM_API int qwm_attention_local(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                                const qwm_strides* st_q, const void* k_loc, const void* v_loc, int64_t n_loc,
+                                const qwm_strides* st_k, const qwm_strides* st_v, float scale, void* out,
+                                const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  qwm::AttnParams p;
+  int s = fill_attn(cfg, cache, q, n_q, st_q, scale, p);
+  if (s) return s;
+  if (cfg->io_dtype != QWM_BF16) return QWM_ERR_UNSUPPORTED;
+  if ((s = check_act(cfg, k_loc, n_loc, st_k)) || (s = check_act(cfg, v_loc, n_loc, st_v))) return s;
+  if (n_loc > ((int64_t)1 << 30)) return QWM_ERR_UNSUPPORTED;
+  if ((s = check_act(cfg, out, n_q, st_out))) return s;
+  if (n_q == 0) return QWM_OK;
+  if (lse && !aligned16(lse)) return QWM_ERR_INVALID_ARG;
+  if (ws_bytes > 0 && (!workspace || !aligned16(workspace))) return QWM_ERR_INVALID_ARG;
+  p.out = out;
+  p.o_head_stride = st_out->head;
+  p.o_token_stride = st_out->token;
+  p.lse = lse;
+  p.n_loc = (int)n_loc;
+  if (n_loc > 0) {
+    p.k_loc = k_loc;
+    p.v_loc = v_loc;
+    p.kl_head_stride = st_k->head;
+    p.kl_token_stride = st_k->token;
+    p.vl_head_stride = st_v->head;
+    p.vl_token_stride = st_v->token;
+  }
+  return run_attention_bf16(cfg, p, workspace, ws_bytes, stream);
 }
 
 QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,

@@ -82,6 +82,12 @@ struct AttnParams {
   uint32_t divF_lo;
   int divF_s;
   int log2T;
+  // optional local chunk (bf16 path): the current chunk's own uncompressed
+  // Keys and Values [H][n_loc][d], attended together with the cache
+  const void* k_loc;
+  const void* v_loc;
+  int64_t kl_head_stride, kl_token_stride, vl_head_stride, vl_token_stride;
+  int n_loc;
   // outputs
   void* out;
   int64_t o_head_stride, o_token_stride;
