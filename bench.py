@@ -324,7 +324,9 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
     # one generation step's attention with the chunk's own keys and values:
     # the query chunk over the full compressed cache and the next frame in
     # bf16 (timed apart from the step, whole call including the merge)
-    F = w.frame_tokens
+    import workloads
+    dt = cfg.torch_dtype
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
     kl = dev(np.stack([workloads.kv_frames(w, h, "k", w.frames, w.frames + 1) for h in range(w.heads)]))
     vl = dev(np.stack([workloads.kv_frames(w, h, "v", w.frames, w.frames + 1) for h in range(w.heads)]))
     ws_l = torch.empty(max(qwm.workspace_bytes(cfg, w.n_tokens + F, w.n_q), 1), dtype=torch.uint8, device="cuda")
@@ -354,6 +356,8 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
         "attention_kernel_ms_final": round(float(attk[-1]), 4),
         "attention_tflops_final": round(float(tf[-1]), 2),
         "attention_tflops_steady_median": round(float(np.median(tf[len(tf) // 2:])), 2),
+        "attention_local_final": {"ms": round(loc_ms, 4), "local_tokens": F, "tflops": round(loc_tf, 2),
+                                  "frac_mfma": round(loc_tf / PEAK_FP16_TFLOPS, 4)},
         "roofline": {"kernel": "attn_bf16_kernel (dequant-attention, final step)", "bound": "mfma",
                      "achieved": round(float(tf[-1]), 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(float(tf[-1]) / PEAK_FP16_TFLOPS, 4), "traffic": None},
