@@ -64,6 +64,28 @@ def append_bytes_per_token_head(w, cfg):
     return 2 * w.head_dim * b_in + idx + 2 * ng * 4 + params + coef
 
 
+def top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, seed, qwm, torch):
+    """Share of (head, query) pairs whose highest-scoring cached token under
+    the rebuilt keys differs from the one under the original keys, for the
+    four modes of the method: QVG (nearest centre, no compensation), QSAC
+    only, PSAC only, and both (QuantWM).  Untimed; each mode calibrates and
+    fills a cache of its own."""
+    import dataclasses
+    dense = qwm.dense_top1(cfg, q, k)
+    modes = {"qvg": (qwm.QVG_MODE, 0), "qsac_only": (0, 0), "psac_only": (qwm.QVG_MODE, w.rank),
+             "quantwm": (0, w.rank)}
+    out = {}
+    for name, (flags, rank) in modes.items():
+        c = dataclasses.replace(cfg, flags=flags, rank=rank)
+        calib = qwm.alloc_calib(c)
+        qwm.calibrate(c, calib, qh, kh, vh, seed=seed, iters=w.kmeans_iters)
+        cache = qwm.Cache(c, calib)
+        qwm.append_kv(cache, k, v)
+        out[name] = round(float((qwm.top1(cache, q) != dense).float().mean()), 5)
+    torch.cuda.synchronize()
+    return out
+
+
 def attn_flops(w, n_q, n_k):
     return 4.0 * n_q * n_k * w.head_dim * w.heads
 
@@ -240,6 +262,8 @@ def main():
     loc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in el]))
     loc_tf = attn_flops(w, w.n_q, w.n_tokens + F) / (loc_ms * 1e-3) / 1e12
 
+    top1 = top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, args.seed, qwm, torch)
+
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
         "metric": METRIC,
@@ -275,6 +299,7 @@ def main():
         "roofline": roofline,
         "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4),
                         "stored_bytes": stored, "original_bytes": original},
+        "top1_shift": top1,
         "top8_energy_mean": round(float(energy.mean()), 4),
         "kernel_source_hash": src_hash,
         "cpu_baseline": None,
