@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling for profiles)")
     ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (default: the step is also captured once per input copy "
+                         "into a HIP graph, and value / ms_per_step come from graph replays)")
     return ap.parse_args()
 
 
@@ -216,6 +219,26 @@ def main():
         step(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    wall_eager = wall
+
+    # The same step captured into a HIP graph (one per rotated input copy:
+    # reset, fused append, attention and its merge pass) and replayed: the
+    # GPU work is identical, the launch gaps between the kernels go away.
+    if not args.no_graph:
+        graphs = []
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     app_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     att_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in range(args.steps)]
@@ -283,7 +306,9 @@ def main():
                    "cached_frames": w.frames, "cached_tokens": w.n_tokens, "query_chunk": w.n_q,
                    "centroids_k": w.c_k, "centroids_v": w.c_v, "top_candidates": w.top_k, "rank": w.rank,
                    "group_tokens": w.group_tokens, "io_dtype": w.io, "parallelism": "single GPU",
-                   "input_copies_rotated": copies},
+                   "input_copies_rotated": copies,
+                   "launch": "eager" if args.no_graph else "hip graph per step (one per input copy)"},
+        "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 4),
         "append": {"ms": round(app_avg, 4), "ktokens_s": round(w.n_tokens / (app_avg * 1e-3) / 1e3, 3),
                    "token_heads_s": round(tok_heads / (app_avg * 1e-3), 1),
                    "algorithmic_gbs": round(app_gbs, 2), "frac_hbm": round(app_gbs / PEAK_HBM_GBS, 4),

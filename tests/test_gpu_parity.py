@@ -308,3 +308,44 @@ def test_local_chunk_edge_cases():
                              o.float().cpu().numpy(), lse.cpu().numpy(), range(cfg.heads))
         say("  empty cache, n_loc=%d: %.3g %.3g" % (n, wo, wl))
         assert wo <= 1.0 and wl <= 1.0
+
+
+def test_graph_replay_equals_eager():
+    """One step (reset, fused append, attention with its merge pass) captured
+    into a HIP graph and replayed three times, with other work and
+    synchronisations between the replays: every replay reproduces the eager
+    cache fields and outputs bit for bit."""
+    import torch
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=2)
+    cfg = P.cfg_of(w)
+    say("case graph_replay")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    cache, calib = P.build_cache(cfg, cal, data["k"], data["v"])
+    q = P.to_dev(data["q"], cfg)
+    o_e, l_e = qwm.attention(cache, q)
+    fields_e = {k: v.clone() for k, v in cache.arrays().items()}
+    kd, vd = P.to_dev(data["k"], cfg), P.to_dev(data["v"], cfg)
+    c2 = qwm.Cache(cfg, calib)
+    o_g, l_g = torch.empty_like(o_e), torch.empty_like(l_e)
+    ws = torch.empty(max(qwm.workspace_bytes(cfg, data["k"].shape[1], q.shape[1]), 1), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c2.reset()
+        qwm.append_kv(c2, kd, vd)
+        qwm.attention(c2, q, out=o_g, lse=l_g, workspace=ws)
+    q_other = P.to_dev(data["q"][:, :100], cfg)
+    for rep in range(3):
+        o_g.zero_()
+        l_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(l_g, l_e), "replay %d" % rep
+        for name, ref in fields_e.items():
+            assert torch.equal(c2.arrays()[name], ref), (rep, name)
+        # other eager work between the replays
+        qwm.attention(cache, q_other)
+        torch.cuda.synchronize()
