@@ -57,7 +57,7 @@ constexpr float kLazy = 8.f;           // log2 headroom before the running max m
 // of units inside one (head, query block) pair is a segment.  A pair cut by a
 // workgroup boundary leaves partial results (O normalised by its own sum, and
 // lse) in workspace slots: slot 2w for workgroup w's first segment, 2w+1 for
-// its last; the combine kernel merges them.  Without a workspace, G equals the
+// its last; the combine kernel merges them, one block per pair and row block.  Without a workspace, G equals the
 // number of pairs and every workgroup takes one whole pair.
 struct Grid {
   int n_qb;        // query blocks per head
@@ -537,45 +537,57 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p
   }
 }
 
-// Merges the partial results of the pair cut by the workgroup boundary
-// w = blockIdx.x + 1 (only the first boundary inside a pair does the work),
-// rows 8 blockIdx.y .. + 7 of the pair's query block, 32 threads per row:
-// o = sum_c exp(lse_c - M) o_c / sum_c exp(lse_c - M), lse = M + log sum.
+// Workgroup w whose units [w U / G, (w + 1) U / G) hold unit x (U >= G).
+__device__ __forceinline__ int wg_of(long long x, const Grid& gr) {
+  int w = (int)(x * gr.G / gr.units);  // its first unit is at most x
+  if (w + 1 < gr.G && (long long)(w + 1) * gr.units / gr.G <= x) ++w;
+  return w;
+}
+
+// Merges the partial results of a pair cut by workgroup boundaries: block
+// (pair, rows 8 blockIdx.y .. + 7 of its query block), 32 threads per row.
+// The contributors are workgroups wa..wb: wa holds the pair in its last
+// segment (its first, when its range starts at the pair), the others in
+// their first.  Online over the contributors, four at a time so that their
+// loads are in flight together:
+//   o = sum_c exp(lse_c - M) o_c / sum_c exp(lse_c - M), lse = M + log sum.
 template <int D>
 __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) {
   constexpr int CPT = D / 32;  // channels per thread
-  const int w = blockIdx.x + 1;
-  const long long nt = gr.ntiles;
-  const long long ub = (long long)w * gr.units / gr.G;  // first unit of workgroup w
-  if (ub % nt == 0) return;                             // boundary at a pair start
-  const long long pair_u = ub - ub % nt;
-  const long long up = (long long)(w - 1) * gr.units / gr.G;
-  if (up > pair_u) return;  // an earlier boundary inside the same pair combines it
-  const int pair = (int)(ub / nt);
+  const int pair = blockIdx.x;
+  const long long x0 = (long long)pair * gr.ntiles;
+  const int wa = wg_of(x0, gr), wb = wg_of(x0 + gr.ntiles - 1, gr);
+  if (wa == wb) return;  // one workgroup took the whole pair and wrote it
   const int qb = pair % gr.n_qb, h = pair / gr.n_qb;
   const int r = blockIdx.y * 8 + (threadIdx.x >> 5);
   const int rows = min(gr.qpb, p.n_q - qb * gr.qpb);
   if (r >= rows) return;
   const int d0 = (threadIdx.x & 31) * CPT;
-  // contributors: w - 1 (the pair is its last segment, or its first when it
-  // starts exactly at the pair), then w, w + 1, ..., v_end - 1, which start
-  // inside the pair (slot 2v: their first segment)
-  const int slot0 = (up == pair_u) ? 2 * (w - 1) : 2 * (w - 1) + 1;
-  int v_end = w;
-  while (v_end < gr.G && (long long)v_end * gr.units / gr.G < pair_u + nt) ++v_end;
-  float M = p.part_ml[(int64_t)slot0 * kSlotRows + r];
-  for (int v = w; v < v_end; ++v) M = fmaxf(M, p.part_ml[(int64_t)(2 * v) * kSlotRows + r]);
-  float tot = 0.f, acc[CPT];
+  const int slot_a = ((long long)wa * gr.units / gr.G >= x0) ? 2 * wa : 2 * wa + 1;
+  float M = -INFINITY, tot = 0.f, acc[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) acc[j] = 0.f;
-  if (M != -INFINITY) {
-    for (int c = -1; c < v_end - w; ++c) {
-      const int64_t pb = (int64_t)(c < 0 ? slot0 : 2 * (w + c)) * kSlotRows + r;
-      const float wt = __expf(p.part_ml[pb] - M);
-      tot += wt;
+  for (int c0 = wa; c0 <= wb; c0 += 4) {
+    float l[4];
+    _Float16 o[4][CPT];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int w = min(c0 + i, wb);
+      const int64_t pb = (int64_t)(w == wa ? slot_a : 2 * w) * kSlotRows + r;
+      l[i] = c0 + i <= wb ? p.part_ml[pb] : -INFINITY;
       const _Float16* src = reinterpret_cast<const _Float16*>(p.part_o) + pb * D + d0;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) acc[j] = fmaf(wt, (float)src[j], acc[j]);
+      for (int j = 0; j < CPT; ++j) o[i][j] = src[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mn = fmaxf(M, l[i]);
+      if (mn == -INFINITY) continue;
+      const float a = __expf(M - mn), b = __expf(l[i] - mn);  // M = -inf: a = 0
+      tot = fmaf(tot, a, b);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) acc[j] = fmaf(acc[j], a, b * (float)o[i][j]);
+      M = mn;
     }
   }
   const int qi = qb * gr.qpb + r;
@@ -621,7 +633,7 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
-  hipLaunchKernelGGL((combine_sk_kernel<D>), dim3(g.G - 1, (g.qpb + 7) / 8), dim3(256), 0, stream, p, g);
+  hipLaunchKernelGGL((combine_sk_kernel<D>), dim3((unsigned)pairs, (g.qpb + 7) / 8), dim3(256), 0, stream, p, g);
   return hipGetLastError();
 }
 
