@@ -71,22 +71,32 @@ def top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, seed, qwm, torch):
     """Share of (head, query) pairs whose highest-scoring cached token under
     the rebuilt keys differs from the one under the original keys, for the
     four modes of the method: QVG (nearest centre, no compensation), QSAC
-    only, PSAC only, and both (QuantWM).  Untimed; each mode calibrates and
-    fills a cache of its own."""
+    only, PSAC only, and both (QuantWM); then QuantWM over compensation ranks
+    r in {0, 4, 8, 16}.  Untimed; each setting calibrates and fills a cache of
+    its own."""
     import dataclasses
     dense = qwm.dense_top1(cfg, q, k)
     modes = {"qvg": (qwm.QVG_MODE, 0), "qsac_only": (0, 0), "psac_only": (qwm.QVG_MODE, w.rank),
              "quantwm": (0, w.rank)}
-    out = {}
+    modes.update({"quantwm_r%d" % r: (0, r) for r in (4, 16) if r != w.rank})
+    # logit MSE on the first 64 queries of every head: mean of (l - l~)^2 over
+    # (head, query, cached token), l = tau q.k with the original keys
+    q64 = q[:, :64]
+    tau = 1.0 / math.sqrt(w.head_dim)
+    ref = tau * torch.bmm(q64.float().contiguous(), k.float().transpose(1, 2).contiguous())
+    top1, mse = {}, {}
     for name, (flags, rank) in modes.items():
         c = dataclasses.replace(cfg, flags=flags, rank=rank)
         calib = qwm.alloc_calib(c)
         qwm.calibrate(c, calib, qh, kh, vh, seed=seed, iters=w.kmeans_iters)
         cache = qwm.Cache(c, calib)
         qwm.append_kv(cache, k, v)
-        out[name] = round(float((qwm.top1(cache, q) != dense).float().mean()), 5)
+        top1[name] = round(float((qwm.top1(cache, q) != dense).float().mean()), 5)
+        lg = qwm.attention_logits(cache, q64)
+        mse[name] = float("%.5g" % float(((lg - ref) ** 2).mean()))
+        del lg
     torch.cuda.synchronize()
-    return out
+    return top1, mse
 
 
 def attn_flops(w, n_q, n_k):
@@ -285,7 +295,7 @@ def main():
     loc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in el]))
     loc_tf = attn_flops(w, w.n_q, w.n_tokens + F) / (loc_ms * 1e-3) / 1e12
 
-    top1 = top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, args.seed, qwm, torch)
+    top1, logit_mse = top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, args.seed, qwm, torch)
 
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
@@ -325,6 +335,7 @@ def main():
         "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4),
                         "stored_bytes": stored, "original_bytes": original},
         "top1_shift": top1,
+        "logit_mse": logit_mse,
         "top8_energy_mean": round(float(energy.mean()), 4),
         "kernel_source_hash": src_hash,
         "cpu_baseline": None,
