@@ -33,6 +33,12 @@
 //    and most tiles skip the rescaling of the accumulators.
 //  * All workgroups of one (head, key range) run on one XCD (workgroups are
 //    dealt to the 8 XCDs round-robin), so their cache reads share its L2.
+//  * Work is split stream-K over (head, query block, key tile) units; query
+//    blocks cut between workgroups leave partial results that a small combine
+//    kernel merges by log-sum-exp.
+//  * One generation step can also attend to the current chunk's own bf16 keys
+//    and values: their tiles continue the key axis after the cache's, in a
+//    separate kernel instantiation (LOCAL).
 #include "qwm_internal.h"
 
 #include <algorithm>
@@ -57,8 +63,9 @@ constexpr float kLazy = 8.f;           // log2 headroom before the running max m
 // of units inside one (head, query block) pair is a segment.  A pair cut by a
 // workgroup boundary leaves partial results (O normalised by its own sum, and
 // lse) in workspace slots: slot 2w for workgroup w's first segment, 2w+1 for
-// its last; the combine kernel merges them, one block per pair and row block.  Without a workspace, G equals the
-// number of pairs and every workgroup takes one whole pair.
+// its last; the combine kernel merges them, one block per pair and row
+// block.  Without a workspace, G equals the number of pairs and every
+// workgroup takes one whole pair.
 struct Grid {
   int n_qb;        // query blocks per head
   int qpb;         // queries per block: a multiple of 32, at most BM
