@@ -72,31 +72,48 @@ def top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, seed, qwm, torch):
     the rebuilt keys differs from the one under the original keys, for the
     four modes of the method: QVG (nearest centre, no compensation), QSAC
     only, PSAC only, and both (QuantWM); then QuantWM over compensation ranks
-    r in {0, 4, 8, 16}.  Untimed; each setting calibrates and fills a cache of
-    its own."""
+    r in {0, 4, 8, 16}, and QuantWM with the stage-2 score taken on the exact
+    INT2 error in the diagonal and in the full quadratic form of Eq. 7.  Each
+    setting calibrates and fills a cache of its own; the append of the three
+    stage-2 scores is timed (HIP events, mean of three appends after one
+    warm-up)."""
     import dataclasses
+
+    import numpy as np
     dense = qwm.dense_top1(cfg, q, k)
     modes = {"qvg": (qwm.QVG_MODE, 0), "qsac_only": (0, 0), "psac_only": (qwm.QVG_MODE, w.rank),
              "quantwm": (0, w.rank)}
     modes.update({"quantwm_r%d" % r: (0, r) for r in (4, 16) if r != w.rank})
+    modes.update({"quantwm_exact": (qwm.EXACT_ERROR, w.rank), "quantwm_full": (qwm.FULL_QUADRATIC, w.rank)})
+    timed = ("quantwm", "quantwm_exact", "quantwm_full")
     # logit MSE on the first 64 queries of every head: mean of (l - l~)^2 over
     # (head, query, cached token), l = tau q.k with the original keys
     q64 = q[:, :64]
     tau = 1.0 / math.sqrt(w.head_dim)
     ref = tau * torch.bmm(q64.float().contiguous(), k.float().transpose(1, 2).contiguous())
-    top1, mse = {}, {}
+    top1, mse, app_ms = {}, {}, {}
     for name, (flags, rank) in modes.items():
         c = dataclasses.replace(cfg, flags=flags, rank=rank)
         calib = qwm.alloc_calib(c)
         qwm.calibrate(c, calib, qh, kh, vh, seed=seed, iters=w.kmeans_iters)
         cache = qwm.Cache(c, calib)
-        qwm.append_kv(cache, k, v)
+        if name in timed:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+            for e in ev:
+                cache.reset()
+                e[0].record()
+                qwm.append_kv(cache, k, v)
+                e[1].record()
+            torch.cuda.synchronize()
+            app_ms[name] = round(float(np.mean([e[0].elapsed_time(e[1]) for e in ev[1:]])), 4)
+        else:
+            qwm.append_kv(cache, k, v)
         top1[name] = round(float((qwm.top1(cache, q) != dense).float().mean()), 5)
         lg = qwm.attention_logits(cache, q64)
         mse[name] = float("%.5g" % float(((lg - ref) ** 2).mean()))
         del lg
     torch.cuda.synchronize()
-    return top1, mse
+    return top1, mse, app_ms
 
 
 def attn_flops(w, n_q, n_k):
@@ -295,7 +312,7 @@ def main():
     loc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in el]))
     loc_tf = attn_flops(w, w.n_q, w.n_tokens + F) / (loc_ms * 1e-3) / 1e12
 
-    top1, logit_mse = top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, args.seed, qwm, torch)
+    top1, logit_mse, stage2_ms = top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, args.seed, qwm, torch)
 
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
@@ -336,6 +353,7 @@ def main():
                         "stored_bytes": stored, "original_bytes": original},
         "top1_shift": top1,
         "logit_mse": logit_mse,
+        "append_ms_by_stage2_score": stage2_ms,
         "top8_energy_mean": round(float(energy.mean()), 4),
         "kernel_source_hash": src_hash,
         "cpu_baseline": None,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define QWM_ABI_VERSION 2
+#define QWM_ABI_VERSION 3
 
 /* status codes */
 #define QWM_OK 0
@@ -68,6 +68,17 @@ extern "C" {
 #define QWM_UNIFORM_SENS 1u   /* QSAC distances and scores with s = 1 */
 #define QWM_NO_RANGE_TERM 2u  /* choose argmin of the stage-1 distance (no INT2 score) */
 #define QWM_QVG_MODE 3u       /* both: nearest Euclidean centre, the QVG baseline */
+/* stage-2 score variants (ablations of the diagonal approximation, [review]
+ * Eq. 7 and Table 10); they act only where stage 2 runs (K_c >= 2 without
+ * QWM_NO_RANGE_TERM).  Both score the candidate's actual INT2 error
+ * e = rho - Q(rho), Q quantizing each of the token's own 16-channel groups
+ * with that group's own (zero, scale) (the tile arithmetic with a one-token
+ * tile): */
+#define QWM_EXACT_ERROR 4u     /* P = sum_j s_j e_j^2 (diagonal form) */
+#define QWM_FULL_QUADRATIC 8u  /* P = e^T M e with the full Query second moment
+                                  M (qwm_calib_import_moment); with
+                                  QWM_UNIFORM_SENS, M = I.  Takes precedence
+                                  over QWM_EXACT_ERROR. */
 
 typedef struct qwm_config {
   int32_t abi_version;      /* QWM_ABI_VERSION */
@@ -82,7 +93,8 @@ typedef struct qwm_config {
   int32_t top_candidates;   /* K_c in [0, 8]: QSAC stage-1 candidates (0: nearest) */
   int32_t rank;             /* r in [0, 16]: PSAC principal directions */
   int32_t io_dtype;         /* QWM_BF16 or QWM_F32 for activations and centres */
-  uint32_t flags;           /* QWM_UNIFORM_SENS | QWM_NO_RANGE_TERM */
+  uint32_t flags;           /* QWM_UNIFORM_SENS | QWM_NO_RANGE_TERM | QWM_EXACT_ERROR |
+                               QWM_FULL_QUADRATIC */
   int32_t reserved;         /* must be 0 */
 } qwm_config;
 
@@ -111,6 +123,10 @@ typedef struct qwm_strides {
  *                       position 2j+1 channel j+8 (j = 0..7)
  *   mu_v16 [H][C_V][d]  the same for mu_v
  *   ut16   [H][16][d]   fp16 U^T in the same channel order; rows >= r are zero
+ *   moment [H][d][d]    fp64 full Query second moment M (QWM_FULL_QUADRATIC
+ *                       only, else 0 bytes; last in the block, written by
+ *                       qwm_calib_import_moment and left alone by
+ *                       qwm_calib_import)
  *
  * Cache block (capacity N = max_frames*F tokens, P = max_frames*ceil(F/T)
  * parameter tiles per head):
@@ -129,7 +145,7 @@ typedef struct qwm_layout_info {
   uint64_t cache_bytes;
   uint64_t token_capacity;
   uint64_t tile_capacity;
-  uint64_t mu_k, mu_v, sens, u, u64, sgroup, norm_kw, norm_k, norm_v, head_max, mu_k16, mu_v16, ut16;
+  uint64_t mu_k, mu_v, sens, u, u64, sgroup, norm_kw, norm_k, norm_v, head_max, mu_k16, mu_v16, ut16, moment;
   uint64_t idx_k, codes_k, params_k, coef, coef_scale, idx_v, codes_v, params_v;
   uint32_t idx_k_bytes, idx_v_bytes;
 } qwm_layout_info;
@@ -197,9 +213,19 @@ int qwm_calib_import(const qwm_config* cfg, void* calib, const float* mu_k,
                      const float* mu_v, const float* sens, const float* u, void* stream);
 
 /*
+ * Loads the full Query second moment m (host fp64 [H][d][d], symmetric,
+ * M = (1/n) sum q q^T per head, [review] Eq. 7) into the calibration block of
+ * a QWM_FULL_QUADRATIC config (other configs: QWM_ERR_INVALID_ARG).
+ * Synchronous on stream.
+ */
+int qwm_calib_import_moment(const qwm_config* cfg, void* calib, const double* m, void* stream);
+
+/*
  * Device-side calibration: copies q_hist [H][n_q][d] and k_hist, v_hist
  * [H][n_kv][d] (io dtype, strided) to the host, runs qwm_calibrate_host and
- * qwm_calib_import.  energy (host, nullable) receives [H] fp64.  Synchronous.
+ * qwm_calib_import (and, for QWM_FULL_QUADRATIC configs, imports
+ * M = (1/n_q) sum q q^T of the same Queries).  energy (host, nullable)
+ * receives [H] fp64.  Synchronous.
  */
 int qwm_calibrate(const qwm_config* cfg, void* calib, const void* q_hist, int64_t n_q,
                   const qwm_strides* st_q, const void* k_hist, const void* v_hist,
@@ -219,7 +245,8 @@ int qwm_cache_init(const qwm_config* cfg, const void* calib, void* base, qwm_cac
  *  QSAC stage 2: P_c = sum_g S_g range_g(rho)^2 with rho = fl32(k - mu_c) and
  *     range_g the max - min over the token's 16 channels of group g; choose
  *     argmin P (ties: smaller D, then lower index).  QWM_NO_RANGE_TERM or
- *     K_c = 0: argmin D.  QWM_UNIFORM_SENS: s = 1.
+ *     K_c = 0: argmin D.  QWM_UNIFORM_SENS: s = 1.  QWM_EXACT_ERROR and
+ *     QWM_FULL_QUADRATIC replace P by the scores defined with those flags.
  *  INT2 per 16 channels x T tokens of one frame: z = fp16(min rho),
  *     s = fp16(fl32(fl32(max - min)/3)); code = #{i in 1..3 : rho >= fl32(z +
  *     (i - 1/2) s)}; s = 0 gives code 0.

@@ -121,9 +121,11 @@ def kmeans(x, c, iters, seed, history=False):
 def calibrate(q_hist, k_hist, v_hist, c_k, c_v, rank, io, seed, iters=10):
     """Per-head calibration.  Inputs are [H, n, d].  Returns a dict of the
     stored fields: mu_k [H,C_K,d], mu_v [H,C_V,d] (float32 holding the storage
-    precision), sens [H,d] float32, u [H,d,r] float32, energy [H] float64."""
+    precision), sens [H,d] float32, u [H,d,r] float32, energy [H] float64,
+    and moment [H,d,d] float64 (the full M, for the full-quadratic stage-2
+    variant)."""
     h_count, _, d = np.shape(q_hist)
-    out = dict(mu_k=[], mu_v=[], sens=[], u=[], energy=[])
+    out = dict(mu_k=[], mu_v=[], sens=[], u=[], energy=[], moment=[])
     for h in range(h_count):
         m = second_moment(q_hist[h])
         u, energy, _ = principal_directions(m, rank)
@@ -134,5 +136,6 @@ def calibrate(q_hist, k_hist, v_hist, c_k, c_v, rank, io, seed, iters=10):
         out["sens"].append(fl32(np.diag(m)))
         out["u"].append(fl32(u).reshape(d, rank))
         out["energy"].append(energy)
+        out["moment"].append(m)
     return {key: np.stack(val) if key != "energy" else np.array(val)
             for key, val in out.items()}

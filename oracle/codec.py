@@ -29,6 +29,18 @@ review summary):
 Flags: UNIFORM_SENS (s = 1), NO_RANGE_TERM (argmin D), QVG_MODE = both, and the
 oracle-only FP32_PARAMS_TEST (z, s kept in float32) used by the INT2 pin.
 
+Stage-2 ablation variants (review summary: Eq. 7 and Table 10, where the full
+quadratic form is compared with the diagonal approximation):
+ * EXACT_ERROR -- instead of the range model, the candidate's actual INT2 error
+   e = rho - Q(rho), where Q quantizes each of the token's own 16-channel groups
+   with that group's parameters (the step-3 arithmetic with a one-token tile;
+   the shared tile's parameters are unknown while its tokens choose), scored
+   by the diagonal form  P_c = sum_j s_j e_j^2.
+ * FULL_QUADRATIC -- the same error scored by the full form of Eq. 7,
+   P_c = e^T M e, with M the Query second moment (with UNIFORM_SENS, M = I).
+   Reading: the variant changes stage 2 only; stage 1 stays the diagonal
+   screen, which the pages name as the screening distance.
+
 Pins (tests/test_oracle_codec.py): invariant (a) QVG_MODE = brute-force nearest
 centre; invariant (b) |rho - rho_hat| <= range/6 + rounding slack; invariant
 (c) rank 0 = QVG reconstruction, rank d removes the Key error up to INT8
@@ -44,6 +56,8 @@ from .numerics import fl32, fp16_of_f32
 UNIFORM_SENS = 1
 NO_RANGE_TERM = 2
 QVG_MODE = UNIFORM_SENS | NO_RANGE_TERM
+EXACT_ERROR = 4
+FULL_QUADRATIC = 8
 FP32_PARAMS_TEST = 16
 
 GROUP = 16
@@ -81,12 +95,48 @@ def range_score(rho, s_group):
     return (rng * rng) @ np.asarray(s_group, np.float64) / 108.0
 
 
-def select_keys(k, mu, sens, top_k, flags):
+def token_int2_error(rho):
+    """e = rho - Q(rho) in float64, Q quantizing each 16-channel group of each
+    row with the row's own parameters: step 3 with a one-token tile, written
+    out over all (row, group) pairs at once."""
+    r = np.asarray(rho, dtype=np.float32)
+    n, d = r.shape
+    g = r.reshape(n, d // GROUP, GROUP)
+    m = g.min(axis=2)
+    mx = g.max(axis=2)
+    width = fl32(mx.astype(np.float64) - m.astype(np.float64))
+    step = fl32(width.astype(np.float64) / 3.0)
+    z = fp16_of_f32(m).astype(np.float64)[..., None]
+    s = fp16_of_f32(step).astype(np.float64)[..., None]
+    code = np.zeros(g.shape, dtype=np.float64)
+    for i in (1, 2, 3):
+        code += g >= fl32(z + (i - 0.5) * s)
+    code = np.where(s == 0, 0.0, code)
+    rhat = fl32(z + code * s)
+    return (g.astype(np.float64) - rhat.astype(np.float64)).reshape(n, d)
+
+
+def exact_error_score(rho, s):
+    """P = sum_j s_j e_j^2 with e the one-token INT2 error (float64)."""
+    e = token_int2_error(rho)
+    return (e * e) @ np.asarray(s, np.float64)
+
+
+def quadratic_error_score(rho, m):
+    """P = e^T M e with e the one-token INT2 error (Eq. 7, full form)."""
+    e = token_int2_error(rho)
+    return np.einsum("ti,ij,tj->t", e, np.asarray(m, np.float64), e)
+
+
+def select_keys(k, mu, sens, top_k, flags, moment=None):
     """QSAC centre choice for each Key row.  Returns (idx, info) where info
-    holds D [n, C], the candidate lists and their P scores."""
+    holds D [n, C], the candidate lists and their P scores.  moment: the
+    Query second moment M [d, d], needed by FULL_QUADRATIC."""
     n, d = k.shape
     c_count = mu.shape[0]
     s = np.ones(d) if flags & UNIFORM_SENS else np.asarray(sens, np.float64)
+    if flags & FULL_QUADRATIC:
+        m_full = np.eye(d) if flags & UNIFORM_SENS else np.asarray(moment, np.float64)
     s_group = group_sums(s)
     dist = weighted_sq_distances(k, mu, s)
     info = dict(D=dist, s=s, s_group=s_group)
@@ -99,7 +149,13 @@ def select_keys(k, mu, sens, top_k, flags):
     cand = order[:, :kc]
     pscore = np.empty((n, kc))
     for j in range(kc):
-        pscore[:, j] = range_score(residual(k, mu[cand[:, j]]), s_group)
+        rho = residual(k, mu[cand[:, j]])
+        if flags & FULL_QUADRATIC:
+            pscore[:, j] = quadratic_error_score(rho, m_full)
+        elif flags & EXACT_ERROR:
+            pscore[:, j] = exact_error_score(rho, s)
+        else:
+            pscore[:, j] = range_score(rho, s_group)
     idx = np.empty(n, dtype=np.int64)
     for t in range(n):
         best = min(range(kc), key=lambda j: (pscore[t, j], dist[t, cand[t, j]], cand[t, j]))
@@ -212,13 +268,14 @@ def psac(k, mu_rows, rho_hat, u):
 
 
 def append_keys(k_new, mu_k, sens, u, frame_tokens, group_tokens, top_k, flags,
-                idx_override=None):
+                idx_override=None, moment=None):
     """Quantize-append of a block of whole frames of Keys for one head.
 
     idx_override: optional {token: centre} dict of decisions to adopt (used by
-    the tie-following checker); everything downstream is recomputed."""
+    the tie-following checker); everything downstream is recomputed.
+    moment: Query second moment M (FULL_QUADRATIC only)."""
     k_new = np.asarray(k_new, dtype=np.float32)
-    idx, info = select_keys(k_new, mu_k, sens, top_k, flags)
+    idx, info = select_keys(k_new, mu_k, sens, top_k, flags, moment)
     if idx_override:
         for t, cidx in idx_override.items():
             idx[t] = cidx

@@ -74,6 +74,8 @@ def build_cache(cfg, cal, k, v, frames_per_call=None):
     import torch
     calib = qwm.alloc_calib(cfg)
     qwm.calib_import(cfg, calib, cal["mu_k"], cal["mu_v"], cal["sens"], cal["u"])
+    if cfg.flags & codec.FULL_QUADRATIC:
+        qwm.calib_import_moment(cfg, calib, cal["moment"])
     cache = qwm.Cache(cfg, calib)
     kd, vd = to_dev(k, cfg), to_dev(v, cfg)
     n = k.shape[1]
@@ -121,8 +123,9 @@ def check_keys_head(cfg, k, cal, h, gpu, stats):
     """Tie-following parity of one head's Keys.  Returns the oracle result
     (with adopted ties) for downstream attention checks."""
     mu, sens, u = cal["mu_k"][h], cal["sens"][h], cal["u"][h]
+    mom = cal["moment"][h] if "moment" in cal else None
     F, T = cfg.frame_tokens, cfg.group_tokens
-    out = codec.append_keys(k, mu, sens, u, F, T, cfg.top_k, cfg.flags)
+    out = codec.append_keys(k, mu, sens, u, F, T, cfg.top_k, cfg.flags, moment=mom)
     m = margins.key_margins(out["info"], cfg.top_k, cfg.flags)
     tie = np.minimum(m["cand"], m["choice"])
     stats.add("k_decisions", k.shape[0])
@@ -134,7 +137,7 @@ def check_keys_head(cfg, k, cal, h, gpu, stats):
     if len(mism):
         stats.add("k_adopted", len(mism))
         out = codec.append_keys(k, mu, sens, u, F, T, cfg.top_k, cfg.flags,
-                                idx_override={int(t): int(g_idx[t]) for t in mism})
+                                idx_override={int(t): int(g_idx[t]) for t in mism}, moment=mom)
     assert np.array_equal(codec.unpack_codes(gpu["codes_k"][h], cfg.head_dim), out["codes"]), "key codes differ"
     assert np.array_equal(gpu["z_k"][h], out["z"]), "key zero points differ"
     assert np.array_equal(gpu["s_k"][h], out["s"]), "key scales differ"

@@ -49,7 +49,8 @@ def cfg_of(w, **kw):
     ("rank", 17, qwm.ERR_UNSUPPORTED),
     ("top_k", 9, qwm.ERR_UNSUPPORTED),
     ("heads", 0, qwm.ERR_INVALID_ARG),
-    ("flags", 8, qwm.ERR_INVALID_ARG),
+    ("flags", 16, qwm.ERR_INVALID_ARG),
+    ("flags", 32, qwm.ERR_INVALID_ARG),
 ])
 def test_config_rejections(field, value, status):
     c = cfg_of(workloads.WORKLOADS["lingbot480p"], **{field: value})
@@ -62,12 +63,31 @@ def test_layout_alignment_and_sizes():
     for name, w in workloads.WORKLOADS.items():
         L = qwm.layout(cfg_of(w))
         for f in ["mu_k", "mu_v", "sens", "u", "u64", "sgroup", "norm_kw", "norm_k", "norm_v", "head_max",
-                  "mu_k16", "mu_v16", "ut16", "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]:
+                  "mu_k16", "mu_v16", "ut16", "moment", "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]:
             assert L[f] % 256 == 0
         assert L["token_capacity"] == w.n_tokens
         assert L["tile_capacity"] == w.frames * -(-w.frame_tokens // w.group_tokens)
         assert L["idx_k_bytes"] == (1 if w.c_k <= 256 else 2)
         assert L["codes_v"] - L["idx_v"] >= w.heads * w.n_tokens * L["idx_v_bytes"]
+        # the full Query second moment is stored only for the full-quadratic score
+        assert L["moment"] == L["calib_bytes"]
+        Lf = qwm.layout(cfg_of(w, flags=qwm.FULL_QUADRATIC))
+        assert Lf["moment"] == L["moment"]
+        assert Lf["calib_bytes"] - Lf["moment"] >= w.heads * w.head_dim ** 2 * 8
+
+
+def test_moment_import_rejections():
+    L = qwm.lib()
+    w = workloads.WORKLOADS["tiny"]
+    m = np.zeros((1, 64, 64))
+    c = cfg_of(w).c()
+    # only full-quadratic configs hold a moment block
+    assert L.qwm_calib_import_moment(ctypes.byref(c), _fake(), m.ctypes.data_as(ctypes.c_void_p), None) == \
+        qwm.ERR_INVALID_ARG
+    cf = cfg_of(w, flags=qwm.FULL_QUADRATIC).c()
+    assert L.qwm_calib_import_moment(ctypes.byref(cf), _fake(), None, None) == qwm.ERR_INVALID_ARG
+    assert L.qwm_calib_import_moment(ctypes.byref(cf), None, m.ctypes.data_as(ctypes.c_void_p), None) == \
+        qwm.ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))

@@ -118,9 +118,19 @@ SMALL = workloads.scaled(W["matrix_game"], heads=2, frames=2)
     ("Kc2", dict(top_k=2)),
     ("Kc8", dict(top_k=8)),
     ("Kc0", dict(top_k=0)),
+    ("exact_error", dict(flags=4)),
+    ("full_quadratic", dict(flags=8)),
+    ("full_quadratic_uniform", dict(flags=9)),
+    ("full_quadratic_Kc8", dict(flags=8, top_k=8)),
 ])
 def test_parity_variants(label, ov):
     run_case(SMALL, ov, iters=3)
+
+
+@pytest.mark.parametrize("flags", [4, 8])
+def test_parity_stage2_variants_f32_d64(flags):
+    """The exact-error scores on the fp32, head_dim 64 instantiation."""
+    run_case(W["tiny"], dict(flags=flags), iters=10)
 
 
 def test_parity_head_dim_64_bf16():

@@ -219,3 +219,91 @@ def test_fp16_of_f32_rne():
     # 1 + 2^-11 is the midpoint between 1 and 1 + 2^-10 in binary16 -> even (1)
     assert fp16_of_f32(np.float32(1 + 2**-11)) == 1.0
     assert fp16_of_f32(np.float32(1 + 3 * 2**-11)) == 1 + 2**-9
+
+
+# ---- stage-2 ablation scores (exact INT2 error; diagonal and full Eq. 7 forms)
+
+def test_stage2_variant_golden_example():
+    g = json.load(open(os.path.join(GOLDEN, "stage2_exact_error.json")))
+    rho = np.array(json.load(open(os.path.join(GOLDEN, "int2_worked.json")))["rho"], np.float32)[None, :]
+    e = codec.token_int2_error(rho)
+    assert e[0].tolist() == g["e"]
+    assert codec.exact_error_score(rho, np.array(g["weights"], np.float64))[0] == g["diagonal_score"]
+    m = np.eye(16) + np.ones((16, 16))
+    assert codec.quadratic_error_score(rho, m)[0] == g["full_score_identity_plus_ones"]
+    assert abs(codec.range_score(rho, [16.0])[0] - g["range_score_uniform"]) < 1e-15
+
+
+def test_token_error_equals_one_token_tiles(tiny):
+    """The per-token error is the tile path's error with one-token tiles."""
+    w, d, cal = tiny
+    rho = codec.residual(d["k"][0], cal["mu_k"][0][np.arange(128) % 16])
+    _, _, _, rho_hat = codec.quantize_residuals(rho, 1, 1)
+    assert np.array_equal(codec.token_int2_error(rho), rho.astype(np.float64) - rho_hat.astype(np.float64))
+
+
+def test_full_quadratic_is_mean_squared_logit_perturbation():
+    """Eq. 7 by brute force: e^T M e equals the mean over the historical
+    queries of (q . e)^2 when M is their second moment."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((300, 64)) * np.exp(rng.standard_normal(64))
+    rho = (rng.standard_normal((20, 64)) * 0.3).astype(np.float32)
+    m = oc.second_moment(q)
+    e = codec.token_int2_error(rho)
+    brute = np.mean((q @ e.T) ** 2, axis=0)
+    got = codec.quadratic_error_score(rho, m)
+    assert np.allclose(got, brute, rtol=1e-12, atol=0)
+
+
+def test_full_quadratic_with_diagonal_moment_is_diagonal_form(tiny):
+    w, d, cal = tiny
+    s = cal["sens"][0].astype(np.float64)
+    k, mu = d["k"][0], cal["mu_k"][0]
+    a, ia = codec.select_keys(k, mu, s, 4, codec.EXACT_ERROR)
+    b, ib = codec.select_keys(k, mu, s, 4, codec.FULL_QUADRATIC, moment=np.diag(s))
+    assert np.array_equal(a, b)
+    assert np.allclose(ia["P"], ib["P"], rtol=1e-12, atol=0)
+    # with UNIFORM_SENS the full form uses M = I: the diagonal form with s = 1
+    a, _ = codec.select_keys(k, mu, s, 4, codec.EXACT_ERROR | codec.UNIFORM_SENS)
+    b, _ = codec.select_keys(k, mu, s, 4, codec.FULL_QUADRATIC | codec.UNIFORM_SENS, moment=np.zeros((64, 64)))
+    assert np.array_equal(a, b)
+
+
+def _one_token_error_py(x, m):
+    """rho = fl32(x - m) and its INT2 error with the token's own parameters per
+    group of 16, one channel at a time with the scalar step-3 functions."""
+    d = len(x)
+    rho = np.array([np.float32(float(x[j]) - float(m[j])) for j in range(d)], np.float32)
+    e = []
+    for g in range(d // 16):
+        blk = rho[16 * g:16 * g + 16]
+        z, s = codec.int2_params(blk)
+        rh = codec.int2_decode(codec.int2_encode(blk, z, s), z, s)
+        e += [float(blk[j]) - float(rh[j]) for j in range(16)]
+    return e
+
+
+@pytest.mark.parametrize("mode", ["exact", "full"])
+def test_invariant_d_stage2_variants_global_argmin(tiny, mode):
+    """K_c = C: the variant's choice is the brute-force argmin over all centres
+    of its score (full form: the mean squared logit perturbation over the
+    historical queries), ties to smaller D then lower index."""
+    w, d, cal = tiny
+    k, mu, s = d["k"][0], cal["mu_k"][0], cal["sens"][0].astype(np.float64)
+    qh = d["q_hist"][0].astype(np.float64)
+    m = oc.second_moment(qh)
+    flags = codec.EXACT_ERROR if mode == "exact" else codec.FULL_QUADRATIC
+    idx, _ = codec.select_keys(k, mu, s, 16, flags, moment=m)
+    for t in range(0, k.shape[0], 7):
+        best = None
+        for c in range(16):
+            e = _one_token_error_py(k[t], mu[c])
+            if mode == "exact":
+                p = sum(s[j] * e[j] ** 2 for j in range(64))
+            else:
+                p = float(np.mean((qh @ np.array(e)) ** 2))
+            dd = sum(s[j] * (float(k[t, j]) - float(mu[c, j])) ** 2 for j in range(64))
+            key = (p, dd, c)
+            if best is None or key[0] < best[0] * (1 - 1e-9) or (abs(key[0] - best[0]) <= 1e-9 * best[0] and key[1:] < best[1:]):
+                best = key
+        assert idx[t] == best[2], (t, idx[t], best)

@@ -16,13 +16,13 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqwm.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGN, ERR_CAPACITY, ERR_STATE, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
-UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE = 1, 2, 3
+UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE, EXACT_ERROR, FULL_QUADRATIC = 1, 2, 3, 4, 8
 
 EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint", "qwm_calibrate_host",
-           "qwm_calib_import", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
+           "qwm_calib_import", "qwm_calib_import_moment", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
            "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention",
            "qwm_attention_timed", "qwm_attention_local", "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
 
@@ -40,7 +40,7 @@ class QwmStrides(ctypes.Structure):
 
 _LAYOUT_FIELDS = ["calib_bytes", "cache_bytes", "token_capacity", "tile_capacity",
                   "mu_k", "mu_v", "sens", "u", "u64", "sgroup", "norm_kw", "norm_k", "norm_v", "head_max",
-                  "mu_k16", "mu_v16", "ut16", "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]
+                  "mu_k16", "mu_v16", "ut16", "moment", "idx_k", "codes_k", "params_k", "coef", "coef_scale", "idx_v", "codes_v", "params_v"]
 
 
 class QwmLayout(ctypes.Structure):
@@ -78,6 +78,7 @@ def lib():
             "qwm_footprint": (ctypes.c_int, [CFG, I64, ctypes.POINTER(U64), ctypes.POINTER(U64), ctypes.POINTER(U64)]),
             "qwm_calibrate_host": (ctypes.c_int, [CFG, P, I64, P, P, I64, U64, I32, P, P, P, P, P]),
             "qwm_calib_import": (ctypes.c_int, [CFG, P, P, P, P, P, P]),
+            "qwm_calib_import_moment": (ctypes.c_int, [CFG, P, P, P]),
             "qwm_calibrate": (ctypes.c_int, [CFG, P, P, I64, ST, P, P, I64, ST, U64, I32, P, P]),
             "qwm_cache_init": (ctypes.c_int, [CFG, P, P, ctypes.POINTER(QwmCache)]),
             "qwm_quantize_append_k": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P]),
@@ -200,6 +201,15 @@ def calib_import(cfg: Config, calib, mu_k, mu_v, sens, u):
     arrs = [_f32(mu_k), _f32(mu_v), _f32(sens), _f32(u if cfg.rank else np.zeros(1))]
     check(lib().qwm_calib_import(ctypes.byref(c), _ptr(calib), *[a.ctypes.data_as(ctypes.c_void_p) for a in arrs],
                                  _stream()))
+
+
+def calib_import_moment(cfg: Config, calib, m):
+    """Full Query second moment [H][d][d] (float64) for FULL_QUADRATIC configs."""
+    c = cfg.c()
+    a = np.ascontiguousarray(m, dtype=np.float64)
+    if a.shape != (cfg.heads, cfg.head_dim, cfg.head_dim):
+        raise ValueError("moment must be [H][d][d]")
+    check(lib().qwm_calib_import_moment(ctypes.byref(c), _ptr(calib), a.ctypes.data_as(ctypes.c_void_p), _stream()))
 
 
 def calibrate(cfg: Config, calib, q_hist, k_hist, v_hist, seed: int, iters: int = 10):

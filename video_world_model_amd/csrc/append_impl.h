@@ -761,30 +761,108 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   int chosen = cand[0];
   if constexpr (KEY && KC > 1) {
     if (p.use_range) {
-      // P_c = sum_g S_g range_g(k - mu_c)^2 for every tracked candidate at once:
-      // each residual group of the row is unpacked once for all K_c centres
-      const double* sg = p.sgroup + (int64_t)h * NG;
       double P[KC];
 #pragma unroll
       for (int i = 0; i < KC; ++i) P[i] = 0.0;
+      if (p.s2mode == 0) {
+        // P_c = sum_g S_g range_g(k - mu_c)^2 for every tracked candidate at once:
+        // each residual group of the row is unpacked once for all K_c centres
+        const double* sg = p.sgroup + (int64_t)h * NG;
 #pragma unroll 1
-      for (int g = 0; g < NG; ++g) {
-        float k[16];
-        load_k16(g, k);
-        const double sgv = p.uniform ? 16.0 : sg[g];
+        for (int g = 0; g < NG; ++g) {
+          float k[16];
+          load_k16(g, k);
+          const double sgv = p.uniform ? 16.0 : sg[g];
 #pragma unroll
-        for (int i = 0; i < KC; ++i) {
-          float m[16];
-          mu_row16(cand[i], g, m);
-          float lo = k[0] - m[0], hi = lo;
+          for (int i = 0; i < KC; ++i) {
+            float m[16];
+            mu_row16(cand[i], g, m);
+            float lo = k[0] - m[0], hi = lo;
+#pragma unroll
+            for (int j = 1; j < 16; ++j) {
+              const float rho = k[j] - m[j];
+              lo = fminf(lo, rho);
+              hi = fmaxf(hi, rho);
+            }
+            const double rg = (double)hi - (double)lo;
+            P[i] = fma(sgv, rg * rg, P[i]);
+          }
+        }
+      } else {
+        // ablation scores on the candidate's actual INT2 error: group g of the
+        // token's residual against centre c, quantized with the group's own
+        // (zero, scale) by the tile arithmetic below; e = rho - rho_hat (exact
+        // in fp64)
+        auto err16 = [&](int c, int g, double (&e)[16]) {
+          float k[16], m[16], rho[16];
+          load_k16(g, k);
+          mu_row16(c, g, m);
+          rho[0] = k[0] - m[0];
+          float lo = rho[0], hi = rho[0];
 #pragma unroll
           for (int j = 1; j < 16; ++j) {
-            const float rho = k[j] - m[j];
-            lo = fminf(lo, rho);
-            hi = fmaxf(hi, rho);
+            rho[j] = k[j] - m[j];
+            lo = fminf(lo, rho[j]);
+            hi = fmaxf(hi, rho[j]);
           }
-          const double rg = (double)hi - (double)lo;
-          P[i] = fma(sgv, rg * rg, P[i]);
+          const float zf = half_bits_to_float(to_half_bits(lo));
+          const float sf = half_bits_to_float(to_half_bits((hi - lo) / 3.0f));
+          const bool zs = sf == 0.f;
+          const float t1 = zs ? INFINITY : zf + 0.5f * sf;
+          const float t2 = zs ? INFINITY : zf + 1.5f * sf;
+          const float t3 = zs ? INFINITY : zf + 2.5f * sf;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float code = (float)((int)(rho[j] >= t1) + (int)(rho[j] >= t2) + (int)(rho[j] >= t3));
+            e[j] = (double)rho[j] - (double)fmaf(code, sf, zf);
+          }
+        };
+        // one candidate at a time (a uniform loop: the error rows stay in
+        // registers with static indices).  s2mode 1, the diagonal form:
+        // P_c = sum_j s_j e_j^2.  s2mode 2, the full form: P_c = e^T M e =
+        // sum_g [e_g^T M_gg e_g + 2 sum_{g' < g} e_g^T M_gg' e_g'], block by
+        // block with both groups' errors recomputed (M is symmetric and read
+        // wave-uniformly).
+        const double* M = p.moment + (int64_t)h * D * D;
+        const bool full = p.s2mode == 2;
+#pragma unroll 1
+        for (int ci = 0; ci < KC; ++ci) {
+          int c = cand[0];
+#pragma unroll
+          for (int i = 1; i < KC; ++i) c = ci == i ? cand[i] : c;
+          double acc = 0.0;
+#pragma unroll 1
+          for (int g = 0; g < NG; ++g) {
+            double eg[16];
+            err16(c, g, eg);
+            if (!full) {
+#pragma unroll
+              for (int j = 0; j < 16; ++j) acc = fma((double)s_lds[16 * g + j] * eg[j], eg[j], acc);
+              continue;
+            }
+#pragma unroll 1
+            for (int gp = 0; gp <= g; ++gp) {
+              double ep[16];
+              if (gp == g) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) ep[j] = eg[j];
+              } else {
+                err16(c, gp, ep);
+              }
+              const double* mb = M + (int64_t)(16 * g) * D + 16 * gp;
+              double blk = 0.0;
+#pragma unroll
+              for (int a = 0; a < 16; ++a) {
+                double t = 0.0;
+#pragma unroll
+                for (int b = 0; b < 16; ++b) t = fma(mb[a * D + b], ep[b], t);
+                blk = fma(eg[a], t, blk);
+              }
+              acc = fma(gp == g ? 1.0 : 2.0, blk, acc);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < KC; ++i) P[i] = ci == i ? acc : P[i];
         }
       }
       double bestP = INFINITY;

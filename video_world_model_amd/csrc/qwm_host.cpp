@@ -40,7 +40,8 @@ int check_config(const qwm_config* c) {
   if (c->num_centroids_k < 1 || c->num_centroids_v < 1) return QWM_ERR_INVALID_ARG;
   if (c->top_candidates < 0 || c->rank < 0 || c->rank > c->head_dim) return QWM_ERR_INVALID_ARG;
   if (c->io_dtype != QWM_BF16 && c->io_dtype != QWM_F32) return QWM_ERR_INVALID_ARG;
-  if (c->flags & ~(QWM_UNIFORM_SENS | QWM_NO_RANGE_TERM)) return QWM_ERR_INVALID_ARG;
+  if (c->flags & ~(QWM_UNIFORM_SENS | QWM_NO_RANGE_TERM | QWM_EXACT_ERROR | QWM_FULL_QUADRATIC))
+    return QWM_ERR_INVALID_ARG;
   if (c->group_channels != 16) return QWM_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return QWM_ERR_UNSUPPORTED;
   const int t = c->group_tokens;
@@ -82,6 +83,7 @@ void fill_layout(const qwm_config* c, qwm_layout_info* L) {
   put(L->mu_k16, H * ck * D * 2);
   put(L->mu_v16, H * cv * D * 2);
   put(L->ut16, H * 16 * D * 2);
+  put(L->moment, (c->flags & QWM_FULL_QUADRATIC) ? H * D * D * 8 : 0);
   L->calib_bytes = o;
   o = 0;
   const uint64_t N = L->token_capacity, P = L->tile_capacity;
@@ -218,12 +220,9 @@ void jacobi_eigen(std::vector<double> a, int d, std::vector<double>& w, std::vec
   for (int i = 0; i < d; ++i) w[i] = A(i, i);
 }
 
-void calibrate_head(const qwm_config* c, const float* qh, int64_t n_q, const float* kh, const float* vh,
-                    int64_t n_kv, uint64_t seed, int iters, int h, float* mu_k, float* mu_v, float* sens,
-                    float* u, double* energy) {
-  const int d = c->head_dim, r = c->rank;
-  // second moment M = (1/n) sum q q^T (fp64)
-  std::vector<double> m((size_t)d * d, 0.0);
+// Query second moment M = (1/n) sum q q^T of one head (fp64, symmetric)
+void second_moment(const float* qh, int64_t n_q, int d, double* m) {
+  std::fill(m, m + (size_t)d * d, 0.0);
   for (int64_t t = 0; t < n_q; ++t) {
     const float* q = qh + (size_t)t * d;
     for (int i = 0; i < d; ++i) {
@@ -236,6 +235,14 @@ void calibrate_head(const qwm_config* c, const float* qh, int64_t n_q, const flo
       m[(size_t)i * d + j] /= (double)n_q;
       m[(size_t)j * d + i] = m[(size_t)i * d + j];
     }
+}
+
+void calibrate_head(const qwm_config* c, const float* qh, int64_t n_q, const float* kh, const float* vh,
+                    int64_t n_kv, uint64_t seed, int iters, int h, float* mu_k, float* mu_v, float* sens,
+                    float* u, double* energy) {
+  const int d = c->head_dim, r = c->rank;
+  std::vector<double> m((size_t)d * d);
+  second_moment(qh, n_q, d, m.data());
   double trace = 0.0;
   for (int i = 0; i < d; ++i) {
     sens[(size_t)h * d + i] = (float)m[(size_t)i * d + i];
@@ -445,7 +452,24 @@ QWM_API int qwm_calib_import(const qwm_config* cfg, void* calib, const float* mu
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
-  e = hipMemcpy(calib, blk.data(), blk.size(), hipMemcpyHostToDevice);
+  // the moment block (last) is not part of this import
+  e = hipMemcpy(calib, blk.data(), (size_t)L.moment, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e);
+  return QWM_OK;
+}
+
+QWM_API int qwm_calib_import_moment(const qwm_config* cfg, void* calib, const double* m, void* stream) {
+  const int st = check_config(cfg);
+  if (st) return st;
+  if (!calib || !m || !(cfg->flags & QWM_FULL_QUADRATIC)) return QWM_ERR_INVALID_ARG;
+  qwm_layout_info L;
+  fill_layout(cfg, &L);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  const size_t bytes = (size_t)cfg->num_heads * cfg->head_dim * cfg->head_dim * 8;
+  e = hipMemcpy(static_cast<unsigned char*>(calib) + L.moment, m, bytes, hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e);
   e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e);
@@ -505,7 +529,11 @@ QWM_API int qwm_calibrate(const qwm_config* cfg, void* calib, const void* q_hist
   st = qwm_calibrate_host(cfg, q.data(), n_q, k.data(), v.data(), n_kv, seed, iters, mk.data(), mv.data(),
                           sens.data(), u.data(), energy);
   if (st) return st;
-  return qwm_calib_import(cfg, calib, mk.data(), mv.data(), sens.data(), u.data(), stream);
+  st = qwm_calib_import(cfg, calib, mk.data(), mv.data(), sens.data(), u.data(), stream);
+  if (st || !(cfg->flags & QWM_FULL_QUADRATIC)) return st;
+  std::vector<double> m((size_t)H * d * d);
+  for (int h = 0; h < H; ++h) second_moment(q.data() + (size_t)h * n_q * d, n_q, d, m.data() + (size_t)h * d * d);
+  return qwm_calib_import_moment(cfg, calib, m.data(), stream);
 }
 
 QWM_API int qwm_cache_init(const qwm_config* cfg, const void* calib, void* base, qwm_cache* cache) {
@@ -564,6 +592,9 @@ int fill_append(const qwm_config* cfg, const qwm_cache* cache, const void* x, in
     p.uniform = (cfg->flags & QWM_UNIFORM_SENS) ? 1 : 0;
     p.use_range = (cfg->flags & QWM_NO_RANGE_TERM) || cfg->top_candidates <= 1 ? 0 : 1;
     p.Kc = p.use_range ? cfg->top_candidates : 1;
+    // stage-2 score: the full form with s = 1 is the diagonal form with s = 1
+    p.s2mode = (cfg->flags & QWM_FULL_QUADRATIC) ? (p.uniform ? 1 : 2) : (cfg->flags & QWM_EXACT_ERROR) ? 1 : 0;
+    p.moment = reinterpret_cast<const double*>(kb + L.moment);
     p.r = cfg->rank;
     p.mu = kb + L.mu_k;
     p.norm_half = reinterpret_cast<const float*>(kb + (p.uniform ? L.norm_k : L.norm_kw));

@@ -29,6 +29,7 @@ struct AppendParams {
   int C, Cpad;         // centres (padded to a multiple of 64: an even number of 32-centre blocks)
   int Kc;              // tracked candidates: K_c for QSAC, 1 for argmin modes
   int use_range;       // QSAC stage 2 active
+  int s2mode;          // stage-2 score: 0 range model, 1 exact error (diagonal), 2 exact error (full M)
   int uniform;         // s = 1
   int r;               // PSAC rank (Keys); 0 for Values
   int64_t Ncap, Pcap;  // token / tile capacity per head
@@ -38,6 +39,7 @@ struct AppendParams {
   const double* u64;      // [H][d][RP] zero-padded
   int rp;                 // RP (row pitch of u64)
   const double* sgroup;   // [H][d/16]
+  const double* moment;   // [H][d][d] full Query second moment (s2mode 2)
   const float* norm_half; // [H][C]  ||mu||^2/2 (weighted or not)
   const float* head_max;  // [H][4]
   int head_max_slot;
