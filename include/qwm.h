@@ -335,6 +335,31 @@ int qwm_attention_local(const qwm_config* cfg, const qwm_cache* cache, const voi
                         const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/*
+ * Attention over a cache kept in calibration epochs.  The Query statistics
+ * and centres come from content already generated ([digest], method
+ * section: training-free, causal statistics of historical Queries); over a
+ * long rollout ([digest] experiments paragraph: 1-minute generation) a caller
+ * may calibrate again from recent frames and start a new cache block with the
+ * new calibration for the frames that follow, so every stored frame keeps
+ * the centres and U it was encoded with.  caches (host array, oldest first)
+ * holds n_caches in [1, 16] such handles of the same cfg, each bound to its
+ * own calibration block; their tokens, then the optional local chunk k_loc,
+ * v_loc as in qwm_attention_local, form the key axis of one softmax:
+ *   k~_t = mu_K^e[idx_t] + rho_hat_t + u^e (coef_t coef_scale_t) for a token
+ *   t of epoch e (v~_t likewise with mu_V^e), out and lse as for
+ *   qwm_attention_local.
+ * One launch; U^T q is formed per epoch.  Every handle needs n_k == n_v (else
+ * QWM_ERR_STATE); empty epochs are allowed.  n_caches > 16:
+ * QWM_ERR_UNSUPPORTED; n_caches < 1 or caches NULL: QWM_ERR_INVALID_ARG.
+ * bf16 activations only.  Workspace: qwm_attention_workspace_size(cfg,
+ * total tokens, n_q).  With n_caches = 1 this is qwm_attention_local.
+ */
+int qwm_attention_epochs(const qwm_config* cfg, const qwm_cache* caches, int32_t n_caches, const void* q,
+                         int64_t n_q, const qwm_strides* st_q, const void* k_loc, const void* v_loc, int64_t n_loc,
+                         const qwm_strides* st_k, const qwm_strides* st_v, float scale, void* out,
+                         const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
 /* The logits l [H][n_q][n_k] fp32 of the same kernel (debug variant), for
  * logit parity checks on small shapes. */
 int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, const void* q,

@@ -28,6 +28,14 @@ the current frames are produced: digest, opening paragraph).  Reading: every
 key of the chunk is visible to every query of the chunk (the chunk is one
 block; no mask inside it).
 
+Calibration epochs (attention_over_epochs): over a long rollout the caller
+may calibrate again from recent content (the statistics come from content
+already generated: digest, method section; 1-minute generation: digest,
+experiments paragraph) and encode the frames that follow with the new
+calibration.  Reading: every stored token keeps the calibration it was
+encoded with, so the epochs' tokens are rebuilt each with their own centres
+and U, and one softmax runs over all of them (and the chunk's own keys).
+
 Pins (tests/test_oracle_attention.py): zero-residual keys reduce to textbook
 softmax attention (PyTorch CPU scaled_dot_product_attention in float64);
 constant V gives o = v; softmax rows sum to one; a split-KV log-sum-exp merge
@@ -35,6 +43,9 @@ equals the unsplit result; brute-force per-query loops on the tiny case.
 attention_with_local: brute-force loops over both key sets; an empty cache
 gives PyTorch's scaled_dot_product_attention over the local keys; local keys
 that repeat the cache's keys leave o unchanged and raise lse by log 2.
+attention_over_epochs: the log-sum-exp merge of each epoch's own attention;
+brute-force loops; each epoch's rebuilt keys obey the PSAC bound along that
+epoch's U (tests/test_oracle_codec.py).
 """
 import numpy as np
 
@@ -110,3 +121,15 @@ def attention_with_local(q, keys, values, k_loc, v_loc, scale=None):
     if k.shape[0] == 0:
         return np.zeros_like(q), np.full(q.shape[0], -np.inf)
     return softmax_attention(q, k, v, scale)
+
+
+def attention_over_epochs(q, epochs, k_loc=None, v_loc=None, scale=None):
+    """o [n_q, d] and lse [n_q] (float64) of one softmax over the rebuilt keys
+    and values of every epoch (a list of (keys, values), each rebuilt with its
+    own calibration) and the chunk's own keys and values (optional)."""
+    d = np.shape(q)[1]
+    keys = [np.asarray(k, np.float64).reshape(-1, d) for k, _ in epochs]
+    values = [np.asarray(v, np.float64).reshape(-1, d) for _, v in epochs]
+    kl = np.zeros((0, d)) if k_loc is None else k_loc
+    vl = np.zeros((0, d)) if v_loc is None else v_loc
+    return attention_with_local(q, np.concatenate(keys), np.concatenate(values), kl, vl, scale)

@@ -156,6 +156,23 @@ def test_append_error_paths_move_no_counter():
     assert L.qwm_attention_local(ctypes.byref(ct), ctypes.byref(ht), _fake(), 32, ctypes.byref(stt), _fake(), _fake(),
                                  64, ctypes.byref(stt), ctypes.byref(stt), ctypes.c_float(0), _fake(0x300000),
                                  ctypes.byref(stt), None, None, 0, None) == qwm.ERR_UNSUPPORTED
+    # calibration epochs: at least one handle, at most 16, each with n_k == n_v
+    hs = (qwm.QwmCache * 17)()
+    for i in range(17):
+        assert L.qwm_cache_init(ctypes.byref(c), _fake(), _fake(0x200000), ctypes.byref(hs[i])) == 0
+    args = (_fake(), 880, ctypes.byref(st), None, None, 0, ctypes.byref(st), ctypes.byref(st), ctypes.c_float(0),
+            _fake(0x300000), ctypes.byref(out_st), None, None, 0, None)
+    assert L.qwm_attention_epochs(ctypes.byref(c), hs, 0, *args) == qwm.ERR_INVALID_ARG
+    assert L.qwm_attention_epochs(ctypes.byref(c), None, 1, *args) == qwm.ERR_INVALID_ARG
+    assert L.qwm_attention_epochs(ctypes.byref(c), hs, 17, *args) == qwm.ERR_UNSUPPORTED
+    hs[2].n_k = 880
+    assert L.qwm_attention_epochs(ctypes.byref(c), hs, 3, *args) == qwm.ERR_STATE
+    hs[2].n_k = 0
+    hs[1].calib = None
+    assert L.qwm_attention_epochs(ctypes.byref(c), hs, 3, *args) == qwm.ERR_INVALID_ARG
+    assert L.qwm_attention_epochs(ctypes.byref(ct), hs, 1, _fake(), 32, ctypes.byref(stt), None, None, 0,
+                                  ctypes.byref(stt), ctypes.byref(stt), ctypes.c_float(0), _fake(0x300000),
+                                  ctypes.byref(stt), None, None, 0, None) == qwm.ERR_UNSUPPORTED
     # wrong abi version in the config
     c2 = cfg_of(w).c()
     c2.abi_version = 99

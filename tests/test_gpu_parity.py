@@ -359,3 +359,100 @@ def test_graph_replay_equals_eager():
         # other eager work between the replays
         qwm.attention(cache, q_other)
         torch.cuda.synchronize()
+
+
+def _epoch_cache(cfg, cal, k, v):
+    """A cache bound to its own calibration, holding k, v (possibly no frames)."""
+    import torch
+    import video_world_model_amd as qwm
+    if k.shape[1]:
+        return P.build_cache(cfg, cal, k, v)[0]
+    calib = qwm.alloc_calib(cfg)
+    qwm.calib_import(cfg, calib, cal["mu_k"], cal["mu_v"], cal["sens"], cal["u"])
+    torch.cuda.synchronize()
+    return qwm.Cache(cfg, calib)
+
+
+@pytest.mark.parametrize("with_local", [True, False])
+def test_epochs_attention(with_local):
+    """Attention over three calibration epochs of one rollout (2, 0 and 1
+    frames, each encoded with a calibration of its own: the first from the
+    history window, the later ones from the last frame before them) and,
+    optionally, the chunk's own keys: one softmax against the oracle, each
+    epoch's tokens rebuilt with its own centres and U.  Stream-K pieces start
+    inside and cross the epoch boundaries."""
+    import video_world_model_amd as qwm
+    from oracle import attention as oa
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=3)
+    cfg = P.cfg_of(w)
+    F = w.frame_tokens
+    say("case epochs_attention local=%s" % with_local)
+    data = case_data(w)
+    spans = [(0, 2), (2, 2), (2, 3)]
+    caches, rebuilt = [], [[] for _ in range(cfg.heads)]
+    for e, (a, b) in enumerate(spans):
+        if e == 0:
+            hist = data
+        else:
+            hist = dict(q_hist=data["q"], k_hist=data["k"][:, (a - 1) * F:a * F],
+                        v_hist=data["v"][:, (a - 1) * F:a * F])
+        cal = P.oracle_calibration(w, hist, cfg, seed=7 + e, iters=3)
+        k_e, v_e = data["k"][:, a * F:b * F], data["v"][:, a * F:b * F]
+        cache = _epoch_cache(cfg, cal, k_e, v_e)
+        caches.append(cache)
+        n = k_e.shape[1]
+        if n == 0:
+            for h in range(cfg.heads):
+                rebuilt[h].append((np.zeros((0, cfg.head_dim)), np.zeros((0, cfg.head_dim))))
+            continue
+        gpu = P.gpu_fields(cache, n)
+        stats = P.Stats()
+        for h in range(cfg.heads):
+            ko = P.check_keys_head(cfg, k_e[h], cal, h, gpu, stats)
+            vo = P.check_values_head(cfg, v_e[h], cal, h, gpu, stats)
+            _, _, kr, vr = P.oracle_attention(cfg, cal, h, ko, vo, data["q"][h][:1])
+            rebuilt[h].append((kr, vr))
+        say("  epoch %d append parity ok: %s" % (e, dict(stats)))
+    q = P.to_dev(data["q"], cfg)
+    if with_local:
+        k_loc = np.stack([workloads.kv_frames(w, h, "k", 3, 4)[:500] for h in range(cfg.heads)])
+        v_loc = np.stack([workloads.kv_frames(w, h, "v", 3, 4)[:500] for h in range(cfg.heads)])
+        o, lse = qwm.attention_epochs(caches, q, P.to_dev(k_loc, cfg), P.to_dev(v_loc, cfg))
+    else:
+        k_loc = v_loc = np.zeros((cfg.heads, 0, cfg.head_dim))
+        o, lse = qwm.attention_epochs(caches, q)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    worst_o, worst_l = 0.0, 0.0
+    for h in range(cfg.heads):
+        oo, ll = oa.attention_over_epochs(data["q"][h], rebuilt[h], k_loc[h].astype(np.float64),
+                                          v_loc[h].astype(np.float64))
+        kall = np.concatenate([kr for kr, _ in rebuilt[h]] + [k_loc[h]])
+        vall = np.concatenate([vr for _, vr in rebuilt[h]] + [v_loc[h]])
+        tol = np.maximum(2e-2, 2.0 ** -11 * np.abs(vall).max(axis=0))[None, :]
+        worst_o = max(worst_o, float(np.max((np.abs(o[h] - oo) - P.bf16_half_ulp(oo)) / tol)))
+        ltol = 1e-3 / np.sqrt(cfg.head_dim) * np.linalg.norm(data["q"][h].astype(np.float64), axis=1) * \
+            np.linalg.norm(kall, axis=1).max()
+        worst_l = max(worst_l, float(np.max(np.abs(lse[h] - ll) / ltol)))
+    say("  epochs: max(|dO| - half ulp)/tol=%.3g max|dlse|/bound=%.3g" % (worst_o, worst_l))
+    assert worst_o <= 1.0 and worst_l <= 1.0
+
+
+def test_epochs_single_equals_local():
+    """One epoch: qwm_attention_epochs is qwm_attention_local, bit for bit."""
+    import torch
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=1)
+    cfg = P.cfg_of(w)
+    say("case epochs_single_equals_local")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    cache, _ = P.build_cache(cfg, cal, data["k"], data["v"])
+    q = P.to_dev(data["q"][:, :300], cfg)
+    kd = P.to_dev(np.stack([workloads.kv_frames(w, h, "k", 1, 2) for h in range(cfg.heads)]), cfg)
+    vd = P.to_dev(np.stack([workloads.kv_frames(w, h, "v", 1, 2) for h in range(cfg.heads)]), cfg)
+    o_a, l_a = qwm.attention_local(cache, q, kd, vd)
+    o_b, l_b = qwm.attention_epochs([cache], q, kd, vd)
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+    o_c, l_c = qwm.attention(cache, q)
+    o_d, l_d = qwm.attention_epochs([cache], q)
+    assert torch.equal(o_c, o_d) and torch.equal(l_c, l_d)

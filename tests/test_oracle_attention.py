@@ -168,3 +168,30 @@ def test_compression_large_configs_exceed_six():
         ratio, _, _ = measures.compression_ratio(w.n_tokens, w.heads, w.head_dim, w.frame_tokens,
                                                  w.group_tokens, w.c_k, w.c_v, w.rank, 2)
         assert ratio > 6.0, (name, ratio)
+
+
+def test_epochs_bruteforce_and_merge():
+    """One softmax over several epochs' keys and the local chunk: per-query
+    loops, and the log-sum-exp merge of each epoch's own attention."""
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((3, 8))
+    eps = [(rng.standard_normal((n, 8)), rng.standard_normal((n, 8))) for n in (5, 0, 3)]
+    kl, vl = rng.standard_normal((2, 8)), rng.standard_normal((2, 8))
+    o, lse = oa.attention_over_epochs(q, eps, kl, vl)
+    keys = [k for e in eps for k in e[0]] + list(kl)
+    vals = [v for e in eps for v in e[1]] + list(vl)
+    for i in range(3):
+        ls = [sum(q[i, j] * kk[j] for j in range(8)) / math.sqrt(8) for kk in keys]
+        m = max(ls)
+        ws = [math.exp(x - m) for x in ls]
+        tot = sum(ws)
+        for j in range(8):
+            assert abs(o[i, j] - sum(wt * vv[j] for wt, vv in zip(ws, vals)) / tot) < 1e-12
+        assert abs(lse[i] - (m + math.log(tot))) < 1e-12
+    parts = [oa.softmax_attention(q, k, v) for k, v in eps if len(k)] + [oa.softmax_attention(q, kl, vl)]
+    om, lm = oa.merge_partials(parts)
+    assert np.allclose(o, om, rtol=0, atol=1e-12) and np.allclose(lse, lm, rtol=0, atol=1e-12)
+    # one epoch and no local keys: plain attention
+    o1, l1 = oa.attention_over_epochs(q, eps[:1])
+    o2, l2 = oa.softmax_attention(q, *eps[0])
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

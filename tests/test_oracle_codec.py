@@ -307,3 +307,32 @@ def test_invariant_d_stage2_variants_global_argmin(tiny, mode):
             if best is None or key[0] < best[0] * (1 - 1e-9) or (abs(key[0] - best[0]) <= 1e-9 * best[0] and key[1:] < best[1:]):
                 best = key
         assert idx[t] == best[2], (t, idx[t], best)
+
+
+def test_epoch_keys_keep_their_own_calibration():
+    """Two calibration epochs of one rollout: each epoch's Keys, encoded and
+    rebuilt with its own centres and U, obey the PSAC bound
+    |U^T (k - k~)| <= sigma/2 along that epoch's U; the other epoch's U does
+    not (the rebuilt keys are tied to the calibration they were encoded with)."""
+    w = workloads.scaled(workloads.WORKLOADS["matrix_game"], heads=1, frames=2)
+    d = workloads.generate(w)
+    F = w.frame_tokens
+    k = d["k"][0]
+    cal0 = oc.calibrate(d["q_hist"], d["k_hist"], d["v_hist"], 32, 32, 8, "bf16", seed=1, iters=2)
+    # the second epoch recalibrates from the first epoch's last frame and the
+    # chunk's queries
+    cal1 = oc.calibrate(d["q"], d["k"][:, :F], d["v"][:, :F], 32, 32, 8, "bf16", seed=2, iters=2)
+    worst_own, worst_other = 0.0, 0.0
+    for e, (cal, other) in enumerate(((cal0, cal1), (cal1, cal0))):
+        ke = k[e * F:(e + 1) * F]
+        out = codec.append_keys(ke, cal["mu_k"][0], cal["sens"][0], cal["u"][0], F, 16, 4, 0)
+        kr = oa.reconstruct_keys(out["idx"], out["codes"], out["z"], out["s"], out["coef"], out["coef_scale"],
+                                 cal["mu_k"][0], cal["u"][0], F, 16)
+        err = ke.astype(np.float64) - kr
+        sig = out["coef_scale"].astype(np.float64)[:, None]
+        own = np.abs(err @ cal["u"][0].astype(np.float64)) - sig / 2
+        oth = np.abs(err @ other["u"][0].astype(np.float64)) - sig / 2
+        worst_own = max(worst_own, float(own.max()))
+        worst_other = max(worst_other, float(oth.max()))
+    assert worst_own <= 1e-4
+    assert worst_other > 1e-2

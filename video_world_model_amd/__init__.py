@@ -24,7 +24,7 @@ UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE, EXACT_ERROR, FULL_QUADRATIC = 1, 2, 3, 4,
 EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint", "qwm_calibrate_host",
            "qwm_calib_import", "qwm_calib_import_moment", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
            "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention",
-           "qwm_attention_timed", "qwm_attention_local", "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
+           "qwm_attention_timed", "qwm_attention_local", "qwm_attention_epochs", "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
 
 
 class QwmConfig(ctypes.Structure):
@@ -91,6 +91,8 @@ def lib():
                                                    ctypes.c_size_t, P, P, P]),
             "qwm_attention_local": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P, I64, ST, ST, F,
                                                    P, ST, P, P, ctypes.c_size_t, P]),
+            "qwm_attention_epochs": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), I32, P, I64, ST, P, P, I64, ST, ST,
+                                                    F, P, ST, P, P, ctypes.c_size_t, P]),
             "qwm_attention_logits": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, P]),
             "qwm_top1": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P]),
             "qwm_dense_top1": (ctypes.c_int, [CFG, P, I64, ST, P, I64, ST, P, P]),
@@ -353,6 +355,35 @@ def attention_local(cache: Cache, q, k_loc, v_loc, out=None, lse=None, workspace
                                     ctypes.byref(sq), _ptr(k_loc), _ptr(v_loc), n_loc, ctypes.byref(sk),
                                     ctypes.byref(sv), scale, _ptr(out), ctypes.byref(so), _ptr(lse),
                                     _ptr(workspace), nb, _stream()))
+    return out, lse
+
+
+def attention_epochs(caches, q, k_loc=None, v_loc=None, out=None, lse=None, workspace=None, scale: float = 0.0):
+    """Attention of the query chunk q over the compressed caches of successive
+    calibration epochs (a list of Cache, oldest first, same Config) and,
+    optionally, the chunk's own keys and values k_loc, v_loc (bf16)."""
+    torch = _torch()
+    cfg = caches[0].cfg
+    n_loc = 0 if k_loc is None else k_loc.shape[1]
+    if n_loc and v_loc.shape[1] != n_loc:
+        raise ValueError("k_loc and v_loc hold different token counts")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(cfg.heads, q.shape[1], dtype=torch.float32, device=q.device)
+    total = sum(c.n_k for c in caches)
+    if workspace is None:
+        nb = workspace_bytes(cfg, total + n_loc, q.shape[1])
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    handles = (QwmCache * len(caches))(*[c.handle for c in caches])
+    c = cfg.c()
+    sq, so = strides(q), strides(out)
+    sk = strides(k_loc) if n_loc else QwmStrides(0, cfg.head_dim)
+    sv = strides(v_loc) if n_loc else QwmStrides(0, cfg.head_dim)
+    nb = workspace.numel() if workspace is not None else 0
+    check(lib().qwm_attention_epochs(ctypes.byref(c), handles, len(caches), _ptr(q), q.shape[1], ctypes.byref(sq),
+                                     _ptr(k_loc), _ptr(v_loc), n_loc, ctypes.byref(sk), ctypes.byref(sv), scale,
+                                     _ptr(out), ctypes.byref(so), _ptr(lse), _ptr(workspace), nb, _stream()))
     return out, lse
 
 

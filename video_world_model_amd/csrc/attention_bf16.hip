@@ -36,9 +36,11 @@
 //  * Work is split stream-K over (head, query block, key tile) units; query
 //    blocks cut between workgroups leave partial results that a small combine
 //    kernel merges by log-sum-exp.
-//  * One generation step can also attend to the current chunk's own bf16 keys
-//    and values: their tiles continue the key axis after the cache's, in a
-//    separate kernel instantiation (LOCAL).
+//  * The key axis can run through several parts in one launch (a separate
+//    kernel instantiation, MULTI): compressed caches of successive calibration
+//    epochs, each rebuilt with its own centres and compensated with its own U
+//    (U^T q is recomputed where a segment enters another epoch), then
+//    optionally the current chunk's own bf16 keys and values.
 #include "qwm_internal.h"
 
 #include <algorithm>
@@ -70,8 +72,8 @@ struct Grid {
   int n_qb;        // query blocks per head
   int qpb;         // queries per block: a multiple of 32, at most BM
   int heads;
-  int ntiles;      // key tiles: the compressed cache's, then the local chunk's
-  int ntc;         // key tiles of the compressed cache (tiles >= ntc are local)
+  int ntiles;      // key tiles: the compressed caches', then the local chunk's
+  int ntc;         // key tiles of the compressed caches
   long long units; // heads * n_qb * ntiles
   int G;           // workgroups with work
   int per_xcd;     // ceil(G / 8): workgroups w of one XCD take a contiguous run
@@ -139,12 +141,13 @@ __device__ __forceinline__ void rebuild16(uint32_t w, uint32_t zs, const uint4& 
 
 // One segment: pair (head, query block), key tiles [tb, te).  slot < 0: the
 // segment covers the pair's whole key range (final output), else partial.
-// LOCAL: the key axis continues with the local chunk's tiles.  Its tile
-// helpers (the *_t lambdas) are used by that instantiation only; the
-// cache-only kernel keeps the loop on key offsets.
-template <int D, bool PS, int NW, bool LOCAL>
-__device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, _Float16* lds, int pair, int tb,
-                                               int te, int slot) {
+// MULTI: the key axis runs through the parts of the table (compressed caches,
+// then the local chunk).  Its tile helpers (the *_t lambdas) are used by that
+// instantiation only; the single-cache kernel keeps the loop on key offsets.
+template <int D, bool PS, int NW, bool MULTI>
+__device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, const PartTable* tp,
+                                               _Float16* lds, int pair, int tb, int te, int slot) {
+  // tp: read by the multi-part instantiation only (null in the other)
   constexpr int NT = 64 * NW;             // threads per workgroup
   constexpr int NG = D / 16;
   constexpr int NKS = NG + (PS ? 1 : 0);  // MFMA k-steps of S (last: PSAC columns)
@@ -169,13 +172,20 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   const bool qvalid = wave_active && qi < p.n_q;
   const int kbeg = tb * BN;
   const int kend = min(p.n_k, te * BN);
-  // local-chunk kernel: tiles [0, ntc) hold the compressed cache, tiles
-  // [ntc, ntiles) the local bf16 keys and values (both from key 0 of their
-  // part); keys past a part's end are masked, prefetches past it read its
-  // last key again
-  auto t_local = [&](int t) { return t >= gr.ntc; };
-  auto t_key0 = [&](int t) { return (t >= gr.ntc ? t - gr.ntc : t) * BN; };
+  // multi-part kernel: part e of the table holds tiles [tile0_e, tile0_e+1),
+  // keys from 0 of its own cache, and tiles from local0 on the local bf16 keys
+  // and values; keys past a part's end are masked, prefetches past it read
+  // its last key again.  part_of(t) is tp->n_parts for a local tile (t is
+  // uniform: scalar code over the table in the kernel arguments).
+  auto part_of = [&](int t) {
+    if (t >= tp->local0) return tp->n_parts;
+    int e = 0;
+    for (int i = 1; i < tp->n_parts; ++i) e += t >= tp->part[i].tile0 ? 1 : 0;
+    return e;
+  };
+  auto t_key0 = [&](int t, int e) { return (t - (e < tp->n_parts ? tp->part[e].tile0 : tp->local0)) * BN; };
   const int ntiles = te - tb;
+  int cur_e = MULTI ? part_of(min(tb, gr.ntiles - 1)) : 0;  // part whose U^T q the Q fragment holds
 
   // ---- Q fragment [q | U^T q] in fp16, paired channel order ----
   h8_t qf[NKS];
@@ -196,7 +206,8 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      const uint16_t* ut = p.ut16 + (int64_t)h * 16 * D;
+      // (local tiles have zero PSAC columns: any part's U serves them)
+      const uint16_t* ut = (MULTI ? tp->part[max(0, min(cur_e, tp->n_parts - 1))].ut16 : p.ut16) + (int64_t)h * 16 * D;
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         h8_t a;
@@ -209,6 +220,26 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       for (int i = 0; i < 8; ++i) qf[NG][i] = (_Float16)acc[i];
     }
   }
+  // U^T q of compressed part e into the Q fragment (multi-part kernel, where a
+  // segment enters another epoch)
+  auto refresh_uq = [&](int e) {
+    if constexpr (MULTI && PS) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      const uint16_t* ut = tp->part[e].ut16 + (int64_t)h * 16 * D;
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        h8_t a;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = (_Float16)0.f;
+        if (l32 < 16) a = *reinterpret_cast<const h8_t*>(ut + l32 * D + 16 * ks + 8 * hf);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[NG][i] = (_Float16)acc[i];
+    }
+  };
 
   // ---- this thread's rebuild items ----
   bool it_v[IPT];
@@ -284,21 +315,58 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       m1[u] = m[1];
     }
   };
-  // tile-indexed loads of the local-chunk kernel: cache fields for compressed
-  // tiles, the bf16 rows themselves (into m0, m1) for local ones
+  // tile-indexed loads of the multi-part kernel: the fields of the tile's own
+  // cache and the centre rows of its own calibration for compressed tiles,
+  // the bf16 rows themselves (into m0, m1) for local ones
   auto load_cache_t = [&](int t, Raw& r) {
     t = min(t, gr.ntiles - 1);
-    if (!t_local(t)) load_cache(t * BN, r);
+    const int e = part_of(t);
+    if (e >= tp->n_parts) return;
+    const CachePart& cp = tp->part[e];
+    const int k0 = t_key0(t, e);
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int key = min(k0 + it_key[u], cp.n_k - 1);
+      const int64_t slot = hN + key;
+      const uint32_t fr = ((uint32_t)key + __umulhi((uint32_t)key, p.divF_lo)) >> p.divF_s;
+      const int tt = (int)fr * p.tpf + ((key - (int)fr * p.F) >> p.log2T);
+      const int g = it_g[u];
+      r.cw[u] = (it_v[u] ? cp.codes_v : cp.codes_k)[slot * NG + g];
+      r.zs[u] = (it_v[u] ? cp.params_v : cp.params_k)[(hP + tt) * NG + g];
+      const void* ib = it_v[u] ? cp.idx_v : cp.idx_k;
+      const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
+      r.idx[u] = bytes == 1 ? (int)static_cast<const uint8_t*>(ib)[slot] : (int)static_cast<const uint16_t*>(ib)[slot];
+    }
+    if constexpr (PS) {
+#pragma unroll
+      for (int v = 0; v < PPT; ++v) {
+        const int64_t slot = hN + min(k0 + pk[v], cp.n_k - 1);
+        const int8_t* cf = cp.coef + slot * p.r;
+        r.pc0[v] = cf[min(pcol[v], p.r - 1)];
+        r.pc1[v] = cf[min(pcol[v] + 1, p.r - 1)];
+        r.psc[v] = cp.coef_scale[slot];
+      }
+    }
   };
   auto load_mu_t = [&](int t, const Raw& r) {
     t = min(t, gr.ntiles - 1);
-    if (!t_local(t)) {
-      load_mu(r);
+    const int e = part_of(t);
+    if (e < tp->n_parts) {
+      const CachePart& cp = tp->part[e];
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) {
+        const int c = min(r.idx[u], (it_v[u] ? p.C_v : p.C_k) - 1);
+        const uint16_t* mrow =
+            it_v[u] ? cp.mu_v16 + ((int64_t)h * p.C_v + c) * D : cp.mu_k16 + ((int64_t)h * p.C_k + c) * D;
+        const uint4* m = reinterpret_cast<const uint4*>(mrow + 16 * it_g[u]);
+        m0[u] = m[0];
+        m1[u] = m[1];
+      }
       return;
     }
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
-      const int kk = min(t_key0(t) + it_key[u], p.n_loc - 1);
+      const int kk = min(t_key0(t, e) + it_key[u], p.n_loc - 1);
       const uint16_t* row = it_v[u] ? static_cast<const uint16_t*>(p.v_loc) + (int64_t)h * p.vl_head_stride +
                                           (int64_t)kk * p.vl_token_stride
                                     : static_cast<const uint16_t*>(p.k_loc) + (int64_t)h * p.kl_head_stride +
@@ -330,10 +398,10 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     }
   };
 
-  // rebuild of tile t in the local-chunk kernel: local rows are converted
+  // rebuild of tile t in the multi-part kernel: local rows are converted
   // from bf16 to fp16 in paired channel order, their PSAC columns are zero
   auto rebuild_t = [&](int buf, const Raw& r, int t) {
-    if (!t_local(min(t, gr.ntiles - 1))) {
+    if (part_of(min(t, gr.ntiles - 1)) < tp->n_parts) {
       rebuild(buf, r);
       return;
     }
@@ -368,7 +436,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
   if (ntiles > 0) {
-    if constexpr (LOCAL) {
+    if constexpr (MULTI) {
       load_cache_t(tb, ra);
       load_mu_t(tb, ra);
       rebuild_t(0, ra, tb);
@@ -386,10 +454,11 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   const int trow = 4 * hf + ((lane & 15) >> 2);             // transposed read: key row in a 16-key chunk
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // and channel position in a 32-channel block
   for (int j = 0; j < ntiles; ++j) {
-    const int t0 = LOCAL ? t_key0(tb + j) : kbeg + j * BN;
-    // end of the keys of this tile's part (local kernel), else of the segment
-    const int tend = LOCAL ? (t_local(tb + j) ? p.n_loc : p.n_k) : kend;
-    if constexpr (LOCAL) {
+    const int ej = MULTI ? part_of(tb + j) : 0;
+    const int t0 = MULTI ? t_key0(tb + j, ej) : kbeg + j * BN;
+    // end of the keys of this tile's part (multi-part kernel), else of the segment
+    const int tend = MULTI ? (ej < tp->n_parts ? tp->part[ej].n_k : p.n_loc) : kend;
+    if constexpr (MULTI) {
       load_mu_t(tb + j + 1, ra);    // centre rows (local tiles: the rows) of tile j+1
       load_cache_t(tb + j + 2, rb);
     } else {
@@ -399,6 +468,12 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     const _Float16* kt = lds + (j & 1) * BUF;
     const _Float16* vt = kt + KT;
     if (__builtin_amdgcn_readfirstlane(wave_active)) {
+      if constexpr (MULTI && PS) {
+        if (ej != cur_e && ej < tp->n_parts) {  // entering another epoch (uniform)
+          refresh_uq(ej);
+          cur_e = ej;
+        }
+      }
       // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
       f32x16 s[2];
       const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -457,7 +532,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
       // rebuild of the next tile into the other buffer: independent VALU work
       // for the scheduler to place among the P V MFMAs
-      if constexpr (LOCAL) rebuild_t((j + 1) & 1, ra, tb + j + 1);
+      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra, tb + j + 1);
       else rebuild((j + 1) & 1, ra);
       // ---- O^T += V~^T P^T ----
 #pragma unroll
@@ -471,7 +546,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
           o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
         }
     } else {
-      if constexpr (LOCAL) rebuild_t((j + 1) & 1, ra, tb + j + 1);
+      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra, tb + j + 1);
       else rebuild((j + 1) & 1, ra);
     }
     ra = rb;
@@ -515,17 +590,17 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   }
 }
 
-// LOCAL: the key axis continues with the local chunk's tiles (a separate
-// instantiation, so the cache-only kernel carries none of their code)
-template <int D, bool PS, int NW, bool LOCAL>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p, Grid gr) {
+// MULTI: the key axis runs through the parts of the table (a separate
+// kernel, so the single-cache one carries none of their code or arguments)
+template <int D, bool PS, int NW, bool MULTI>
+__device__ __forceinline__ void attn_bf16_body(const AttnParams& p, const Grid& gr, const PartTable* tbl) {
   constexpr int BUF = BN * (D + 24) + BN * (D + 32);
   __shared__ __align__(16) _Float16 lds[2 * BUF];
   const int bid = blockIdx.x;
   const int w = (bid & 7) * gr.per_xcd + (bid >> 3);
   if (w >= gr.G) return;
   if (gr.ntiles == 0) {  // no keys at all: every pair writes zeros and lse = -inf
-    attend_segment<D, PS, NW, LOCAL>(p, gr, lds, w, 0, 0, -1);
+    attend_segment<D, PS, NW, MULTI>(p, gr, tbl, lds, w, 0, 0, -1);
     return;
   }
   const long long u0 = (long long)w * gr.units / gr.G;
@@ -537,11 +612,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p
     const int tb = (int)(u % gr.ntiles);
     const int te = (int)min<long long>(gr.ntiles, tb + (u1 - u));
     const int slot = (tb == 0 && te == gr.ntiles) ? -1 : (first ? 2 * w : 2 * w + 1);
-    attend_segment<D, PS, NW, LOCAL>(p, gr, lds, pair, tb, te, slot);
+    attend_segment<D, PS, NW, MULTI>(p, gr, tbl, lds, pair, tb, te, slot);
     u += te - tb;
     first = false;
     __syncthreads();  // the next segment's first rebuild reuses buffer 0
   }
+}
+
+template <int D, bool PS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p, Grid gr) {
+  attn_bf16_body<D, PS, NW, false>(p, gr, nullptr);
+}
+
+template <int D, bool PS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_multi_kernel(AttnParams p, Grid gr, PartTable tbl) {
+  attn_bf16_body<D, PS, NW, true>(p, gr, &tbl);
 }
 
 // Workgroup w whose units [w U / G, (w + 1) U / G) hold unit x (U >= G).
@@ -606,7 +691,7 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) 
 }
 
 template <int D, bool PS>
-hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
+hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream, const PartTable* parts) {
   constexpr int BM = 32 * kWaves;               // queries per workgroup
   const int max_wg = kAttnBf16MaxWorkgroups * 8 / kWaves;  // one CU's worth per 8 waves
   Grid g;
@@ -614,8 +699,20 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
   g.n_qb = (p.n_q + BM - 1) / BM;
   const int per = (p.n_q + g.n_qb - 1) / g.n_qb;  // balance the query blocks
   g.qpb = (per + 31) / 32 * 32;
-  g.ntc = (p.n_k + BN - 1) / BN;
-  g.ntiles = g.ntc + (p.n_loc + BN - 1) / BN;
+  // the multi-part kernel's table: tile0 of each part, then local0
+  PartTable tbl{};
+  int ntc = (p.n_k + BN - 1) / BN;
+  if (parts) {
+    tbl = *parts;
+    ntc = 0;
+    for (int e = 0; e < tbl.n_parts; ++e) {
+      tbl.part[e].tile0 = ntc;
+      ntc += (tbl.part[e].n_k + BN - 1) / BN;
+    }
+    tbl.local0 = ntc;
+  }
+  g.ntc = ntc;
+  g.ntiles = ntc + (p.n_loc + BN - 1) / BN;
   const long long pairs = (long long)g.n_qb * heads;
   g.units = pairs * g.ntiles;
   if (g.ntiles == 0 || !p.part_o) {
@@ -633,10 +730,11 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
     const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(p.ev_begin), stream);
     if (er != hipSuccess) return er;
   }
-  if (p.n_loc > 0)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves, true>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
+  if (parts)
+    hipLaunchKernelGGL((attn_bf16_multi_kernel<D, PS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g,
+                       tbl);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves, false>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
@@ -646,9 +744,11 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return p.r > 0 ? launch_t<128, true>(p, heads, stream) : launch_t<128, false>(p, heads, stream);
-  return p.r > 0 ? launch_t<64, true>(p, heads, stream) : launch_t<64, false>(p, heads, stream);
+hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream,
+                                 const PartTable* parts) {
+  if (head_dim == 128)
+    return p.r > 0 ? launch_t<128, true>(p, heads, stream, parts) : launch_t<128, false>(p, heads, stream, parts);
+  return p.r > 0 ? launch_t<64, true>(p, heads, stream, parts) : launch_t<64, false>(p, heads, stream, parts);
 }
 
 }  // namespace qwm

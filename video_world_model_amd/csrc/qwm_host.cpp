@@ -750,14 +750,16 @@ QWM_API size_t qwm_attention_workspace_size(const qwm_config* cfg, int64_t n_tok
 
 // bf16 activations: stream-K partials when the workspace holds them, else one
 // whole (head, query block) per workgroup
-int run_attention_bf16(const qwm_config* cfg, qwm::AttnParams& p, void* workspace, size_t ws_bytes, void* stream) {
+int run_attention_bf16(const qwm_config* cfg, qwm::AttnParams& p, void* workspace, size_t ws_bytes, void* stream,
+                       const qwm::PartTable* parts = nullptr) {
   if (p.n_k + p.n_loc > 0 && ws_bytes >= bf16_partial_bytes(cfg)) {
     const size_t rows = 2 * (size_t)qwm::kAttnBf16MaxWorkgroups * qwm::kAttnBf16Queries;
     p.part_o = static_cast<float*>(workspace);  // holds fp16 rows on this path
     p.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
                                          align256(rows * (size_t)cfg->head_dim * 2));
   }
-  hipError_t e = qwm::launch_attention(p, cfg->num_heads, cfg->head_dim, false, static_cast<hipStream_t>(stream));
+  hipError_t e = parts ? qwm::launch_attention_bf16(p, cfg->num_heads, cfg->head_dim, static_cast<hipStream_t>(stream), parts)
+                       : qwm::launch_attention(p, cfg->num_heads, cfg->head_dim, false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return QWM_OK;
 }
@@ -799,21 +801,59 @@ QWM_API int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, c
   return QWM_OK;
 }
 
-QWM_API int qwm_attention_local(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
-                                const qwm_strides* st_q, const void* k_loc, const void* v_loc, int64_t n_loc,
-                                const qwm_strides* st_k, const qwm_strides* st_v, float scale, void* out,
-                                const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes,
-                                void* stream) {
+namespace {
+
+// The fields of one compressed cache for the multi-part attention kernel.
+void fill_part(const qwm_layout_info& L, const qwm_cache* c, qwm::CachePart& cp) {
+  const unsigned char* cb = static_cast<const unsigned char*>(c->base);
+  const unsigned char* kb = static_cast<const unsigned char*>(c->calib);
+  cp.idx_k = cb + L.idx_k;
+  cp.idx_v = cb + L.idx_v;
+  cp.codes_k = reinterpret_cast<const uint32_t*>(cb + L.codes_k);
+  cp.codes_v = reinterpret_cast<const uint32_t*>(cb + L.codes_v);
+  cp.params_k = reinterpret_cast<const uint32_t*>(cb + L.params_k);
+  cp.params_v = reinterpret_cast<const uint32_t*>(cb + L.params_v);
+  cp.coef = reinterpret_cast<const int8_t*>(cb + L.coef);
+  cp.coef_scale = reinterpret_cast<const uint16_t*>(cb + L.coef_scale);
+  cp.mu_k16 = reinterpret_cast<const uint16_t*>(kb + L.mu_k16);
+  cp.mu_v16 = reinterpret_cast<const uint16_t*>(kb + L.mu_v16);
+  cp.ut16 = reinterpret_cast<const uint16_t*>(kb + L.ut16);
+  cp.n_k = (int)c->n_k;
+  cp.tile0 = 0;
+}
+
+// Attention of one query chunk over the compressed caches of successive
+// epochs (oldest first) and optionally the chunk's own keys and values, in one
+// softmax (bf16 activations).
+int attention_parts(const qwm_config* cfg, const qwm_cache* caches, int32_t n_caches, const void* q, int64_t n_q,
+                    const qwm_strides* st_q, const void* k_loc, const void* v_loc, int64_t n_loc,
+                    const qwm_strides* st_k, const qwm_strides* st_v, float scale, void* out,
+                    const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (!caches || n_caches < 1) return QWM_ERR_INVALID_ARG;
   qwm::AttnParams p;
-  int s = fill_attn(cfg, cache, q, n_q, st_q, scale, p);
+  int s = fill_attn(cfg, &caches[0], q, n_q, st_q, scale, p);
   if (s) return s;
+  if (n_caches > qwm::kMaxParts) return QWM_ERR_UNSUPPORTED;
+  qwm_layout_info L;
+  fill_layout(cfg, &L);
+  int64_t total = 0;
+  for (int e = 0; e < n_caches; ++e) {
+    const qwm_cache* c = &caches[e];
+    if (!c->base || !c->calib || c->abi_version != QWM_ABI_VERSION) return QWM_ERR_INVALID_ARG;
+    if (c->n_k != c->n_v || c->n_k < 0 || c->n_k > (int64_t)L.token_capacity) return QWM_ERR_STATE;
+    total += c->n_k;
+  }
   if (cfg->io_dtype != QWM_BF16) return QWM_ERR_UNSUPPORTED;
   if ((s = check_act(cfg, k_loc, n_loc, st_k)) || (s = check_act(cfg, v_loc, n_loc, st_v))) return s;
-  if (n_loc > ((int64_t)1 << 30)) return QWM_ERR_UNSUPPORTED;
+  if (n_loc > ((int64_t)1 << 30) || total > ((int64_t)1 << 30)) return QWM_ERR_UNSUPPORTED;
   if ((s = check_act(cfg, out, n_q, st_out))) return s;
   if (n_q == 0) return QWM_OK;
   if (lse && !aligned16(lse)) return QWM_ERR_INVALID_ARG;
   if (ws_bytes > 0 && (!workspace || !aligned16(workspace))) return QWM_ERR_INVALID_ARG;
+  qwm::PartTable tbl{};
+  tbl.n_parts = n_caches;
+  for (int e = 0; e < n_caches; ++e) fill_part(L, &caches[e], tbl.part[e]);
+  p.n_k = (int)total;
   p.out = out;
   p.o_head_stride = st_out->head;
   p.o_token_stride = st_out->token;
@@ -827,7 +867,28 @@ QWM_API int qwm_attention_local(const qwm_config* cfg, const qwm_cache* cache, c
     p.vl_head_stride = st_v->head;
     p.vl_token_stride = st_v->token;
   }
-  return run_attention_bf16(cfg, p, workspace, ws_bytes, stream);
+  // one cache and no local keys: the single-cache kernel
+  return run_attention_bf16(cfg, p, workspace, ws_bytes, stream, (n_caches == 1 && n_loc == 0) ? nullptr : &tbl);
+}
+
+}  // namespace
+
+QWM_API int qwm_attention_local(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                                const qwm_strides* st_q, const void* k_loc, const void* v_loc, int64_t n_loc,
+                                const qwm_strides* st_k, const qwm_strides* st_v, float scale, void* out,
+                                const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  return attention_parts(cfg, cache, 1, q, n_q, st_q, k_loc, v_loc, n_loc, st_k, st_v, scale, out, st_out, lse,
+                         workspace, ws_bytes, stream);
+}
+
+QWM_API int qwm_attention_epochs(const qwm_config* cfg, const qwm_cache* caches, int32_t n_caches, const void* q,
+                                 int64_t n_q, const qwm_strides* st_q, const void* k_loc, const void* v_loc,
+                                 int64_t n_loc, const qwm_strides* st_k, const qwm_strides* st_v, float scale,
+                                 void* out, const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return attention_parts(cfg, caches, n_caches, q, n_q, st_q, k_loc, v_loc, n_loc, st_k, st_v, scale, out, st_out,
+                         lse, workspace, ws_bytes, stream);
 }
 
 QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,

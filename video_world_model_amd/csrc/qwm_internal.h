@@ -107,6 +107,31 @@ struct AttnParams {
   float* part_ml;        // [splits][H][n_q] (bf16 path: [slots][rows]) natural-log lse
 };
 
+// Parts of the key axis of one attention call: compressed caches (epochs,
+// each with its own calibration), then optionally the local chunk.  Each part
+// starts at a tile boundary; a part's keys run from 0 to n_k in its own cache.
+constexpr int kMaxParts = 16;
+struct CachePart {
+  const void* idx_k;
+  const void* idx_v;
+  const uint32_t* codes_k;
+  const uint32_t* codes_v;
+  const uint32_t* params_k;
+  const uint32_t* params_v;
+  const int8_t* coef;
+  const uint16_t* coef_scale;
+  const uint16_t* mu_k16;
+  const uint16_t* mu_v16;
+  const uint16_t* ut16;
+  int n_k;    // tokens of the part
+  int tile0;  // its first key tile
+};
+struct PartTable {
+  CachePart part[kMaxParts];
+  int n_parts;  // compressed parts (tiles from local0 on are the local chunk's)
+  int local0;
+};
+
 QWM_HIDDEN hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io,
                                     bool key, hipStream_t stream);
 // Keys and Values of the same frames in one launch (pk, pv as for launch_append)
@@ -114,8 +139,11 @@ QWM_HIDDEN hipError_t launch_append_kv(const AppendParams& pk, const AppendParam
                                        bool f32io, hipStream_t stream);
 QWM_HIDDEN hipError_t launch_attention(const AttnParams& p, int heads, int head_dim, bool f32io,
                                        hipStream_t stream);
-// bf16 activations, softmax attention only (no logits / top-1 export)
-QWM_HIDDEN hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream);
+// bf16 activations, softmax attention only (no logits / top-1 export); with a
+// part table (several compressed caches and / or the local chunk: p.n_loc),
+// the key axis runs through the parts in order
+QWM_HIDDEN hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream,
+                                            const PartTable* parts = nullptr);
 QWM_HIDDEN hipError_t launch_combine(const AttnParams& p, int heads, int head_dim, bool f32io, hipStream_t stream);
 // queries per workgroup of the bf16 attention kernel, and its workgroup cap
 // (one per CU of the MI355X); the partial-result workspace holds two slots of
