@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling for profiles)")
     ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--epoch-frames", type=int, default=24,
+                    help="1-minute rollout: also run it with a calibration epoch every this many frames "
+                         "(0: skip)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the step is also captured once per input copy "
                          "into a HIP graph, and value / ms_per_step come from graph replays)")
@@ -217,7 +220,7 @@ def main():
     reset = cache.reset
 
     if args.config == "minute":
-        return rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torch)
+        return rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torch, qh)
 
     # per step: append (one kernel), attention call, attention kernel alone
     # (events recorded by the library around its main kernel, on its stream)
@@ -372,7 +375,51 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torch):
+def rollout_epochs(args, w, cfg, ks, vs, q, qh, out, lse, ws, qwm, torch):
+    """The 1-minute rollout with calibration epochs: every `epoch_frames`
+    frames the library calibrates again (Query statistics from the query
+    history, centres from the last cached frame) and the frames that follow go
+    to a new cache bound to that calibration; each step attends over all
+    epochs' caches in one launch.  Calibration is host work and untimed (its
+    mean wall time is reported apart)."""
+    import numpy as np
+    F, E = w.frame_tokens, args.epoch_frames
+    n_ep = -(-w.frames // E)
+    import dataclasses
+    ecfg = dataclasses.replace(cfg, max_frames=E)
+    caches, cal_s = [], []
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(w.frames)]
+    for f in range(w.frames):
+        if f % E == 0:
+            t0 = time.perf_counter()
+            calib = qwm.alloc_calib(ecfg)
+            if f == 0:
+                src = (qh, ks[0][:, :F], vs[0][:, :F])
+            else:
+                src = (qh, ks[0][:, (f - 1) * F:f * F], vs[0][:, (f - 1) * F:f * F])
+            qwm.calibrate(ecfg, calib, *src, seed=args.seed + f, iters=w.kmeans_iters)
+            caches.append(qwm.Cache(ecfg, calib))
+            cal_s.append(time.perf_counter() - t0)
+            print("[bench] epoch %d calibrated at frame %d in %.1fs" % (len(caches) - 1, f, cal_s[-1]),
+                  file=sys.stderr, flush=True)
+        e = ev[f]
+        e[0].record()
+        qwm.append_kv(caches[-1], ks[0][:, f * F:(f + 1) * F], vs[0][:, f * F:(f + 1) * F])
+        e[1].record()
+        qwm.attention_epochs(caches, q, out=out, lse=lse, workspace=ws)
+        e[2].record()
+    torch.cuda.synchronize()
+    app = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    att = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    tf_final = attn_flops(w, w.n_q, w.frames * F) / (att[-1] * 1e-3) / 1e12
+    return {"epoch_frames": E, "epochs": n_ep, "append_ms_median": round(float(np.median(app)), 4),
+            "attention_ms_median": round(float(np.median(att)), 4),
+            "attention_ms_final": round(float(att[-1]), 4), "attention_tflops_final": round(float(tf_final), 2),
+            "calibration_s_mean": round(float(np.mean(cal_s)), 3),
+            "launch": "one attention launch over all epochs' caches per step (combine pass included)"}
+
+
+def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torch, qh):
     """1-minute horizon: per generation step append one frame (K and V), then
     attend the query chunk over everything cached so far."""
     import numpy as np
@@ -443,6 +490,8 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
         "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4)},
         "cpu_baseline": None,
     }
+    if args.epoch_frames:
+        res["calibration_epochs"] = rollout_epochs(args, w, cfg, ks, vs, q, qh, out, lse, ws, qwm, torch)
     print(json.dumps(res), flush=True)
 
 

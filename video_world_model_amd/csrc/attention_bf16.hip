@@ -44,6 +44,7 @@
 #include "qwm_internal.h"
 
 #include <algorithm>
+#include <climits>
 
 namespace qwm {
 namespace {
@@ -139,6 +140,25 @@ __device__ __forceinline__ void rebuild16(uint32_t w, uint32_t zs, const uint4& 
   o1 = make_uint4(r[4], r[5], r[6], r[7]);
 }
 
+// Part e of the table.  Constant-offset reads only: a dynamic index into the
+// by-value kernel argument would make the compiler copy the whole table to
+// scratch memory.
+__device__ __forceinline__ CachePart part_at(const PartTable& t, int e) {
+  switch (e) {
+#define QWM_PART_CASE(E) \
+    case E:              \
+      return t.part[E];
+    QWM_PART_CASE(0) QWM_PART_CASE(1) QWM_PART_CASE(2) QWM_PART_CASE(3)
+    QWM_PART_CASE(4) QWM_PART_CASE(5) QWM_PART_CASE(6) QWM_PART_CASE(7)
+    QWM_PART_CASE(8) QWM_PART_CASE(9) QWM_PART_CASE(10) QWM_PART_CASE(11)
+    QWM_PART_CASE(12) QWM_PART_CASE(13) QWM_PART_CASE(14)
+#undef QWM_PART_CASE
+    default:
+      return t.part[kMaxParts - 1];
+  }
+}
+static_assert(kMaxParts == 16, "part_at covers 16 parts");
+
 // One segment: pair (head, query block), key tiles [tb, te).  slot < 0: the
 // segment covers the pair's whole key range (final output), else partial.
 // MULTI: the key axis runs through the parts of the table (compressed caches,
@@ -175,17 +195,36 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   // multi-part kernel: part e of the table holds tiles [tile0_e, tile0_e+1),
   // keys from 0 of its own cache, and tiles from local0 on the local bf16 keys
   // and values; keys past a part's end are masked, prefetches past it read
-  // its last key again.  part_of(t) is tp->n_parts for a local tile (t is
-  // uniform: scalar code over the table in the kernel arguments).
-  auto part_of = [&](int t) {
-    if (t >= tp->local0) return tp->n_parts;
-    int e = 0;
-    for (int i = 1; i < tp->n_parts; ++i) e += t >= tp->part[i].tile0 ? 1 : 0;
-    return e;
+  // its last key again.  A cursor over the parts (scalar values) moves
+  // forward with the prefetch stage, since a segment visits its tiles in
+  // order; each prefetched tile carries its part's values (Meta) to the
+  // stages after it.
+  struct Cursor {
+    const unsigned char* cb;  // cache block of part e
+    const unsigned char* kb;  // its calibration block (the last compressed part's, for local tiles)
+    int e, t0, t1, n_k;       // part (n_parts: the local chunk), its tiles [t0, t1), its keys
   };
-  auto t_key0 = [&](int t, int e) { return (t - (e < tp->n_parts ? tp->part[e].tile0 : tp->local0)) * BN; };
+  Cursor cu{nullptr, nullptr, -1, 0, INT_MIN, 0};
+  auto seek = [&](int t) {
+    while (cu.e < tp->n_parts && t >= cu.t1) {
+      ++cu.e;
+      if (cu.e < tp->n_parts) {
+        const CachePart cp = part_at(*tp, cu.e);
+        cu.cb = cp.cache;
+        cu.kb = cp.calib;
+        cu.n_k = cp.n_k;
+        cu.t0 = cp.tile0;
+        cu.t1 = cu.e + 1 < tp->n_parts ? part_at(*tp, cu.e + 1).tile0 : tp->local0;
+      } else {
+        cu.n_k = p.n_loc;
+        cu.t0 = tp->local0;
+        cu.t1 = INT_MAX;
+      }
+    }
+  };
   const int ntiles = te - tb;
-  int cur_e = MULTI ? part_of(min(tb, gr.ntiles - 1)) : 0;  // part whose U^T q the Q fragment holds
+  if constexpr (MULTI) seek(min(tb, gr.ntiles - 1));
+  int cur_e = MULTI ? cu.e : 0;  // part whose U^T q the Q fragment holds
 
   // ---- Q fragment [q | U^T q] in fp16, paired channel order ----
   h8_t qf[NKS];
@@ -207,7 +246,8 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
       // (local tiles have zero PSAC columns: any part's U serves them)
-      const uint16_t* ut = (MULTI ? tp->part[max(0, min(cur_e, tp->n_parts - 1))].ut16 : p.ut16) + (int64_t)h * 16 * D;
+      const uint16_t* ut =
+          (MULTI ? reinterpret_cast<const uint16_t*>(cu.kb + tp->ut16) : p.ut16) + (int64_t)h * 16 * D;
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         h8_t a;
@@ -222,12 +262,12 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   }
   // U^T q of compressed part e into the Q fragment (multi-part kernel, where a
   // segment enters another epoch)
-  auto refresh_uq = [&](int e) {
+  auto refresh_uq = [&](const unsigned char* kb) {
     if constexpr (MULTI && PS) {
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      const uint16_t* ut = tp->part[e].ut16 + (int64_t)h * 16 * D;
+      const uint16_t* ut = reinterpret_cast<const uint16_t*>(kb + tp->ut16) + (int64_t)h * 16 * D;
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         h8_t a;
@@ -269,11 +309,16 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   // Compressed-cache fields of one tile for this thread's items; they stream
   // from HBM, so they are loaded two tiles ahead of their rebuild.  The centre
   // rows (a small, L2-resident table) are loaded one tile ahead.
+  struct Meta {               // multi-part kernel: the tile's part
+    const unsigned char* kb;  // calibration block
+    int e, k0, tend;          // part index, first key of the tile in it, its end
+  };
   struct Raw {
     uint32_t cw[IPT], zs[IPT];
     int idx[IPT];
     int8_t pc0[PPT], pc1[PPT];
     uint16_t psc[PPT];
+    Meta m;
   };
   Raw ra, rb;  // tiles j+1 and j+2
   uint4 m0[IPT], m1[IPT];
@@ -320,44 +365,52 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   // the bf16 rows themselves (into m0, m1) for local ones
   auto load_cache_t = [&](int t, Raw& r) {
     t = min(t, gr.ntiles - 1);
-    const int e = part_of(t);
-    if (e >= tp->n_parts) return;
-    const CachePart& cp = tp->part[e];
-    const int k0 = t_key0(t, e);
+    seek(t);
+    r.m.kb = cu.kb;
+    r.m.e = cu.e;
+    r.m.k0 = (t - cu.t0) * BN;
+    r.m.tend = cu.n_k;
+    if (cu.e >= tp->n_parts) return;
+    const unsigned char* cb = cu.cb;
+    const uint32_t* codes_k = reinterpret_cast<const uint32_t*>(cb + tp->codes_k);
+    const uint32_t* codes_v = reinterpret_cast<const uint32_t*>(cb + tp->codes_v);
+    const uint32_t* params_k = reinterpret_cast<const uint32_t*>(cb + tp->params_k);
+    const uint32_t* params_v = reinterpret_cast<const uint32_t*>(cb + tp->params_v);
+    const int k0 = r.m.k0, nk = cu.n_k;
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
-      const int key = min(k0 + it_key[u], cp.n_k - 1);
+      const int key = min(k0 + it_key[u], nk - 1);
       const int64_t slot = hN + key;
       const uint32_t fr = ((uint32_t)key + __umulhi((uint32_t)key, p.divF_lo)) >> p.divF_s;
       const int tt = (int)fr * p.tpf + ((key - (int)fr * p.F) >> p.log2T);
       const int g = it_g[u];
-      r.cw[u] = (it_v[u] ? cp.codes_v : cp.codes_k)[slot * NG + g];
-      r.zs[u] = (it_v[u] ? cp.params_v : cp.params_k)[(hP + tt) * NG + g];
-      const void* ib = it_v[u] ? cp.idx_v : cp.idx_k;
+      r.cw[u] = (it_v[u] ? codes_v : codes_k)[slot * NG + g];
+      r.zs[u] = (it_v[u] ? params_v : params_k)[(hP + tt) * NG + g];
+      const unsigned char* ib = cb + (it_v[u] ? tp->idx_v : tp->idx_k);
       const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
-      r.idx[u] = bytes == 1 ? (int)static_cast<const uint8_t*>(ib)[slot] : (int)static_cast<const uint16_t*>(ib)[slot];
+      r.idx[u] = bytes == 1 ? (int)ib[slot] : (int)reinterpret_cast<const uint16_t*>(ib)[slot];
     }
     if constexpr (PS) {
+      const int8_t* coef = reinterpret_cast<const int8_t*>(cb + tp->coef);
+      const uint16_t* coef_scale = reinterpret_cast<const uint16_t*>(cb + tp->coef_scale);
 #pragma unroll
       for (int v = 0; v < PPT; ++v) {
-        const int64_t slot = hN + min(k0 + pk[v], cp.n_k - 1);
-        const int8_t* cf = cp.coef + slot * p.r;
+        const int64_t slot = hN + min(k0 + pk[v], nk - 1);
+        const int8_t* cf = coef + slot * p.r;
         r.pc0[v] = cf[min(pcol[v], p.r - 1)];
         r.pc1[v] = cf[min(pcol[v] + 1, p.r - 1)];
-        r.psc[v] = cp.coef_scale[slot];
+        r.psc[v] = coef_scale[slot];
       }
     }
   };
-  auto load_mu_t = [&](int t, const Raw& r) {
-    t = min(t, gr.ntiles - 1);
-    const int e = part_of(t);
-    if (e < tp->n_parts) {
-      const CachePart& cp = tp->part[e];
+  auto load_mu_t = [&](const Raw& r) {
+    if (r.m.e < tp->n_parts) {
+      const uint16_t* mk = reinterpret_cast<const uint16_t*>(r.m.kb + tp->mu_k16);
+      const uint16_t* mv = reinterpret_cast<const uint16_t*>(r.m.kb + tp->mu_v16);
 #pragma unroll
       for (int u = 0; u < IPT; ++u) {
         const int c = min(r.idx[u], (it_v[u] ? p.C_v : p.C_k) - 1);
-        const uint16_t* mrow =
-            it_v[u] ? cp.mu_v16 + ((int64_t)h * p.C_v + c) * D : cp.mu_k16 + ((int64_t)h * p.C_k + c) * D;
+        const uint16_t* mrow = it_v[u] ? mv + ((int64_t)h * p.C_v + c) * D : mk + ((int64_t)h * p.C_k + c) * D;
         const uint4* m = reinterpret_cast<const uint4*>(mrow + 16 * it_g[u]);
         m0[u] = m[0];
         m1[u] = m[1];
@@ -366,7 +419,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     }
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
-      const int kk = min(t_key0(t, e) + it_key[u], p.n_loc - 1);
+      const int kk = min(r.m.k0 + it_key[u], p.n_loc - 1);
       const uint16_t* row = it_v[u] ? static_cast<const uint16_t*>(p.v_loc) + (int64_t)h * p.vl_head_stride +
                                           (int64_t)kk * p.vl_token_stride
                                     : static_cast<const uint16_t*>(p.k_loc) + (int64_t)h * p.kl_head_stride +
@@ -400,8 +453,8 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 
   // rebuild of tile t in the multi-part kernel: local rows are converted
   // from bf16 to fp16 in paired channel order, their PSAC columns are zero
-  auto rebuild_t = [&](int buf, const Raw& r, int t) {
-    if (part_of(min(t, gr.ntiles - 1)) < tp->n_parts) {
+  auto rebuild_t = [&](int buf, const Raw& r) {
+    if (r.m.e < tp->n_parts) {
       rebuild(buf, r);
       return;
     }
@@ -435,11 +488,13 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
+  Meta mj{};  // multi-part kernel: the part of tile j
   if (ntiles > 0) {
     if constexpr (MULTI) {
       load_cache_t(tb, ra);
-      load_mu_t(tb, ra);
-      rebuild_t(0, ra, tb);
+      load_mu_t(ra);
+      rebuild_t(0, ra);
+      mj = ra.m;
       load_cache_t(tb + 1, ra);
     } else {
       load_cache(kbeg, ra);
@@ -454,12 +509,11 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   const int trow = 4 * hf + ((lane & 15) >> 2);             // transposed read: key row in a 16-key chunk
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // and channel position in a 32-channel block
   for (int j = 0; j < ntiles; ++j) {
-    const int ej = MULTI ? part_of(tb + j) : 0;
-    const int t0 = MULTI ? t_key0(tb + j, ej) : kbeg + j * BN;
+    const int t0 = MULTI ? mj.k0 : kbeg + j * BN;
     // end of the keys of this tile's part (multi-part kernel), else of the segment
-    const int tend = MULTI ? (ej < tp->n_parts ? tp->part[ej].n_k : p.n_loc) : kend;
+    const int tend = MULTI ? mj.tend : kend;
     if constexpr (MULTI) {
-      load_mu_t(tb + j + 1, ra);    // centre rows (local tiles: the rows) of tile j+1
+      load_mu_t(ra);                // centre rows (local tiles: the rows) of tile j+1
       load_cache_t(tb + j + 2, rb);
     } else {
       load_mu(ra);                  // centre rows of tile j+1
@@ -469,9 +523,9 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     const _Float16* vt = kt + KT;
     if (__builtin_amdgcn_readfirstlane(wave_active)) {
       if constexpr (MULTI && PS) {
-        if (ej != cur_e && ej < tp->n_parts) {  // entering another epoch (uniform)
-          refresh_uq(ej);
-          cur_e = ej;
+        if (mj.e != cur_e && mj.e < tp->n_parts) {  // entering another epoch (uniform)
+          refresh_uq(mj.kb);
+          cur_e = mj.e;
         }
       }
       // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
@@ -532,7 +586,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
       // rebuild of the next tile into the other buffer: independent VALU work
       // for the scheduler to place among the P V MFMAs
-      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra, tb + j + 1);
+      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra);
       else rebuild((j + 1) & 1, ra);
       // ---- O^T += V~^T P^T ----
 #pragma unroll
@@ -546,9 +600,10 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
           o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
         }
     } else {
-      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra, tb + j + 1);
+      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra);
       else rebuild((j + 1) & 1, ra);
     }
+    if constexpr (MULTI) mj = ra.m;
     ra = rb;
     __syncthreads();
   }

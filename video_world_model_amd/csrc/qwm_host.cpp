@@ -803,21 +803,10 @@ QWM_API int qwm_attention_timed(const qwm_config* cfg, const qwm_cache* cache, c
 
 namespace {
 
-// The fields of one compressed cache for the multi-part attention kernel.
-void fill_part(const qwm_layout_info& L, const qwm_cache* c, qwm::CachePart& cp) {
-  const unsigned char* cb = static_cast<const unsigned char*>(c->base);
-  const unsigned char* kb = static_cast<const unsigned char*>(c->calib);
-  cp.idx_k = cb + L.idx_k;
-  cp.idx_v = cb + L.idx_v;
-  cp.codes_k = reinterpret_cast<const uint32_t*>(cb + L.codes_k);
-  cp.codes_v = reinterpret_cast<const uint32_t*>(cb + L.codes_v);
-  cp.params_k = reinterpret_cast<const uint32_t*>(cb + L.params_k);
-  cp.params_v = reinterpret_cast<const uint32_t*>(cb + L.params_v);
-  cp.coef = reinterpret_cast<const int8_t*>(cb + L.coef);
-  cp.coef_scale = reinterpret_cast<const uint16_t*>(cb + L.coef_scale);
-  cp.mu_k16 = reinterpret_cast<const uint16_t*>(kb + L.mu_k16);
-  cp.mu_v16 = reinterpret_cast<const uint16_t*>(kb + L.mu_v16);
-  cp.ut16 = reinterpret_cast<const uint16_t*>(kb + L.ut16);
+// One compressed cache as a part of the multi-part attention kernel.
+void fill_part(const qwm_cache* c, qwm::CachePart& cp) {
+  cp.cache = static_cast<const unsigned char*>(c->base);
+  cp.calib = static_cast<const unsigned char*>(c->calib);
   cp.n_k = (int)c->n_k;
   cp.tile0 = 0;
 }
@@ -852,7 +841,18 @@ int attention_parts(const qwm_config* cfg, const qwm_cache* caches, int32_t n_ca
   if (ws_bytes > 0 && (!workspace || !aligned16(workspace))) return QWM_ERR_INVALID_ARG;
   qwm::PartTable tbl{};
   tbl.n_parts = n_caches;
-  for (int e = 0; e < n_caches; ++e) fill_part(L, &caches[e], tbl.part[e]);
+  for (int e = 0; e < n_caches; ++e) fill_part(&caches[e], tbl.part[e]);
+  tbl.idx_k = (int64_t)L.idx_k;
+  tbl.idx_v = (int64_t)L.idx_v;
+  tbl.codes_k = (int64_t)L.codes_k;
+  tbl.codes_v = (int64_t)L.codes_v;
+  tbl.params_k = (int64_t)L.params_k;
+  tbl.params_v = (int64_t)L.params_v;
+  tbl.coef = (int64_t)L.coef;
+  tbl.coef_scale = (int64_t)L.coef_scale;
+  tbl.mu_k16 = (int64_t)L.mu_k16;
+  tbl.mu_v16 = (int64_t)L.mu_v16;
+  tbl.ut16 = (int64_t)L.ut16;
   p.n_k = (int)total;
   p.out = out;
   p.o_head_stride = st_out->head;

@@ -110,26 +110,22 @@ struct AttnParams {
 // Parts of the key axis of one attention call: compressed caches (epochs,
 // each with its own calibration), then optionally the local chunk.  Each part
 // starts at a tile boundary; a part's keys run from 0 to n_k in its own cache.
+// Every part has the same configuration, so the fields sit at the same byte
+// offsets inside each cache block and each calibration block.
 constexpr int kMaxParts = 16;
 struct CachePart {
-  const void* idx_k;
-  const void* idx_v;
-  const uint32_t* codes_k;
-  const uint32_t* codes_v;
-  const uint32_t* params_k;
-  const uint32_t* params_v;
-  const int8_t* coef;
-  const uint16_t* coef_scale;
-  const uint16_t* mu_k16;
-  const uint16_t* mu_v16;
-  const uint16_t* ut16;
-  int n_k;    // tokens of the part
-  int tile0;  // its first key tile
+  const unsigned char* cache;  // cache block
+  const unsigned char* calib;  // its calibration block
+  int n_k;                     // tokens of the part
+  int tile0;                   // its first key tile
 };
 struct PartTable {
   CachePart part[kMaxParts];
   int n_parts;  // compressed parts (tiles from local0 on are the local chunk's)
   int local0;
+  // byte offsets in the cache block, then in the calibration block
+  int64_t idx_k, idx_v, codes_k, codes_v, params_k, params_v, coef, coef_scale;
+  int64_t mu_k16, mu_v16, ut16;
 };
 
 QWM_HIDDEN hipError_t launch_append(const AppendParams& p, int heads, int head_dim, bool f32io,
