@@ -45,6 +45,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 namespace qwm {
 namespace {
@@ -162,8 +163,9 @@ static_assert(kMaxParts == 16, "part_at covers 16 parts");
 // One segment: pair (head, query block), key tiles [tb, te).  slot < 0: the
 // segment covers the pair's whole key range (final output), else partial.
 // MULTI: the key axis runs through the parts of the table (compressed caches,
-// then the local chunk).  Its tile helpers (the *_t lambdas) are used by that
-// instantiation only; the single-cache kernel keeps the loop on key offsets.
+// then the local chunk).  The segment then runs the pipelined tile loop once
+// per part it touches, with that part's fields fixed (the loop restarts at a
+// part boundary), and forms U^T q again on entering another epoch.
 template <int D, bool PS, int NW, bool MULTI>
 __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, const PartTable* tp,
                                                _Float16* lds, int pair, int tb, int te, int slot) {
@@ -190,41 +192,37 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   const bool wave_active = wave * 32 < gr.qpb && q0 < p.n_q;  // wave-uniform
   const int qi = q0 + l32;
   const bool qvalid = wave_active && qi < p.n_q;
-  const int kbeg = tb * BN;
-  const int kend = min(p.n_k, te * BN);
-  // multi-part kernel: part e of the table holds tiles [tile0_e, tile0_e+1),
-  // keys from 0 of its own cache, and tiles from local0 on the local bf16 keys
-  // and values; keys past a part's end are masked, prefetches past it read
-  // its last key again.  A cursor over the parts (scalar values) moves
-  // forward with the prefetch stage, since a segment visits its tiles in
-  // order; each prefetched tile carries its part's values (Meta) to the
-  // stages after it.
-  struct Cursor {
-    const unsigned char* cb;  // cache block of part e
-    const unsigned char* kb;  // its calibration block (the last compressed part's, for local tiles)
-    int e, t0, t1, n_k;       // part (n_parts: the local chunk), its tiles [t0, t1), its keys
+
+  // Fields of the compressed cache the tile loop reads: the call's own cache,
+  // or one part of the table.
+  struct Fields {
+    const void* idx_k;
+    const void* idx_v;
+    const uint32_t* codes_k;
+    const uint32_t* codes_v;
+    const uint32_t* params_k;
+    const uint32_t* params_v;
+    const int8_t* coef;
+    const uint16_t* coef_scale;
+    const uint16_t* mu_k16;
+    const uint16_t* mu_v16;
+    const uint16_t* ut16;
   };
-  Cursor cu{nullptr, nullptr, -1, 0, INT_MIN, 0};
-  auto seek = [&](int t) {
-    while (cu.e < tp->n_parts && t >= cu.t1) {
-      ++cu.e;
-      if (cu.e < tp->n_parts) {
-        const CachePart cp = part_at(*tp, cu.e);
-        cu.cb = cp.cache;
-        cu.kb = cp.calib;
-        cu.n_k = cp.n_k;
-        cu.t0 = cp.tile0;
-        cu.t1 = cu.e + 1 < tp->n_parts ? part_at(*tp, cu.e + 1).tile0 : tp->local0;
-      } else {
-        cu.n_k = p.n_loc;
-        cu.t0 = tp->local0;
-        cu.t1 = INT_MAX;
-      }
-    }
+  auto fields_of = [&](const CachePart& cp) {
+    Fields f;
+    f.idx_k = cp.cache + tp->idx_k;
+    f.idx_v = cp.cache + tp->idx_v;
+    f.codes_k = reinterpret_cast<const uint32_t*>(cp.cache + tp->codes_k);
+    f.codes_v = reinterpret_cast<const uint32_t*>(cp.cache + tp->codes_v);
+    f.params_k = reinterpret_cast<const uint32_t*>(cp.cache + tp->params_k);
+    f.params_v = reinterpret_cast<const uint32_t*>(cp.cache + tp->params_v);
+    f.coef = reinterpret_cast<const int8_t*>(cp.cache + tp->coef);
+    f.coef_scale = reinterpret_cast<const uint16_t*>(cp.cache + tp->coef_scale);
+    f.mu_k16 = reinterpret_cast<const uint16_t*>(cp.calib + tp->mu_k16);
+    f.mu_v16 = reinterpret_cast<const uint16_t*>(cp.calib + tp->mu_v16);
+    f.ut16 = reinterpret_cast<const uint16_t*>(cp.calib + tp->ut16);
+    return f;
   };
-  const int ntiles = te - tb;
-  if constexpr (MULTI) seek(min(tb, gr.ntiles - 1));
-  int cur_e = MULTI ? cu.e : 0;  // part whose U^T q the Q fragment holds
 
   // ---- Q fragment [q | U^T q] in fp16, paired channel order ----
   h8_t qf[NKS];
@@ -241,33 +239,14 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       qf[ks] = h8_t{bf_to_h(a.x & 0xffffu), bf_to_h(b.x & 0xffffu), bf_to_h(a.x >> 16), bf_to_h(b.x >> 16),
                     bf_to_h(a.y & 0xffffu), bf_to_h(b.y & 0xffffu), bf_to_h(a.y >> 16), bf_to_h(b.y >> 16)};
     }
+  }
+  // U^T q of one calibration into the PSAC k-step of the Q fragment
+  auto form_uq = [&](const uint16_t* ut16) {
     if constexpr (PS) {
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      // (local tiles have zero PSAC columns: any part's U serves them)
-      const uint16_t* ut =
-          (MULTI ? reinterpret_cast<const uint16_t*>(cu.kb + tp->ut16) : p.ut16) + (int64_t)h * 16 * D;
-#pragma unroll
-      for (int ks = 0; ks < NG; ++ks) {
-        h8_t a;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = (_Float16)0.f;
-        if (l32 < 16) a = *reinterpret_cast<const h8_t*>(ut + l32 * D + 16 * ks + 8 * hf);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[NG][i] = (_Float16)acc[i];
-    }
-  }
-  // U^T q of compressed part e into the Q fragment (multi-part kernel, where a
-  // segment enters another epoch)
-  auto refresh_uq = [&](const unsigned char* kb) {
-    if constexpr (MULTI && PS) {
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      const uint16_t* ut = reinterpret_cast<const uint16_t*>(kb + tp->ut16) + (int64_t)h * 16 * D;
+      const uint16_t* ut = ut16 + (int64_t)h * 16 * D;
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         h8_t a;
@@ -280,6 +259,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       for (int i = 0; i < 8; ++i) qf[NG][i] = (_Float16)acc[i];
     }
   };
+  if constexpr (!MULTI) form_uq(p.ut16);
 
   // ---- this thread's rebuild items ----
   bool it_v[IPT];
@@ -303,182 +283,19 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 
   const int64_t hN = (int64_t)h * p.Ncap;
   const int64_t hP = (int64_t)h * p.Pcap;
-  // keys past the end read the last key of the range (finite data, masked scores)
-  auto slot_of = [&](int key) { return hN + min(key, kend - 1); };
 
   // Compressed-cache fields of one tile for this thread's items; they stream
   // from HBM, so they are loaded two tiles ahead of their rebuild.  The centre
   // rows (a small, L2-resident table) are loaded one tile ahead.
-  struct Meta {               // multi-part kernel: the tile's part
-    const unsigned char* kb;  // calibration block
-    int e, k0, tend;          // part index, first key of the tile in it, its end
-  };
   struct Raw {
     uint32_t cw[IPT], zs[IPT];
     int idx[IPT];
     int8_t pc0[PPT], pc1[PPT];
     uint16_t psc[PPT];
-    Meta m;
   };
-  Raw ra, rb;  // tiles j+1 and j+2
   uint4 m0[IPT], m1[IPT];
-
-  auto load_cache = [&](int t0, Raw& r) {
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int key = min(t0 + it_key[u], kend - 1);
-      const int64_t slot = hN + key;
-      const uint32_t fr = ((uint32_t)key + __umulhi((uint32_t)key, p.divF_lo)) >> p.divF_s;
-      const int tt = (int)fr * p.tpf + ((key - (int)fr * p.F) >> p.log2T);
-      const int g = it_g[u];
-      r.cw[u] = (it_v[u] ? p.codes_v : p.codes_k)[slot * NG + g];
-      r.zs[u] = (it_v[u] ? p.params_v : p.params_k)[(hP + tt) * NG + g];
-      const void* ib = it_v[u] ? p.idx_v : p.idx_k;
-      const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
-      r.idx[u] = bytes == 1 ? (int)static_cast<const uint8_t*>(ib)[slot] : (int)static_cast<const uint16_t*>(ib)[slot];
-    }
-    if constexpr (PS) {
-      // unconditional loads (columns past the rank are masked at the rebuild),
-      // so that nothing waits for them before the rebuild
-#pragma unroll
-      for (int v = 0; v < PPT; ++v) {
-        const int64_t slot = slot_of(t0 + pk[v]);
-        const int8_t* cf = p.coef + slot * p.r;
-        r.pc0[v] = cf[min(pcol[v], p.r - 1)];
-        r.pc1[v] = cf[min(pcol[v] + 1, p.r - 1)];
-        r.psc[v] = p.coef_scale[slot];
-      }
-    }
-  };
-  auto load_mu = [&](const Raw& r) {
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int c = min(r.idx[u], (it_v[u] ? p.C_v : p.C_k) - 1);
-      const uint16_t* mrow = it_v[u] ? p.mu_v16 + ((int64_t)h * p.C_v + c) * D : p.mu_k16 + ((int64_t)h * p.C_k + c) * D;
-      const uint4* m = reinterpret_cast<const uint4*>(mrow + 16 * it_g[u]);
-      m0[u] = m[0];
-      m1[u] = m[1];
-    }
-  };
-  // tile-indexed loads of the multi-part kernel: the fields of the tile's own
-  // cache and the centre rows of its own calibration for compressed tiles,
-  // the bf16 rows themselves (into m0, m1) for local ones
-  auto load_cache_t = [&](int t, Raw& r) {
-    t = min(t, gr.ntiles - 1);
-    seek(t);
-    r.m.kb = cu.kb;
-    r.m.e = cu.e;
-    r.m.k0 = (t - cu.t0) * BN;
-    r.m.tend = cu.n_k;
-    if (cu.e >= tp->n_parts) return;
-    const unsigned char* cb = cu.cb;
-    const uint32_t* codes_k = reinterpret_cast<const uint32_t*>(cb + tp->codes_k);
-    const uint32_t* codes_v = reinterpret_cast<const uint32_t*>(cb + tp->codes_v);
-    const uint32_t* params_k = reinterpret_cast<const uint32_t*>(cb + tp->params_k);
-    const uint32_t* params_v = reinterpret_cast<const uint32_t*>(cb + tp->params_v);
-    const int k0 = r.m.k0, nk = cu.n_k;
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int key = min(k0 + it_key[u], nk - 1);
-      const int64_t slot = hN + key;
-      const uint32_t fr = ((uint32_t)key + __umulhi((uint32_t)key, p.divF_lo)) >> p.divF_s;
-      const int tt = (int)fr * p.tpf + ((key - (int)fr * p.F) >> p.log2T);
-      const int g = it_g[u];
-      r.cw[u] = (it_v[u] ? codes_v : codes_k)[slot * NG + g];
-      r.zs[u] = (it_v[u] ? params_v : params_k)[(hP + tt) * NG + g];
-      const unsigned char* ib = cb + (it_v[u] ? tp->idx_v : tp->idx_k);
-      const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
-      r.idx[u] = bytes == 1 ? (int)ib[slot] : (int)reinterpret_cast<const uint16_t*>(ib)[slot];
-    }
-    if constexpr (PS) {
-      const int8_t* coef = reinterpret_cast<const int8_t*>(cb + tp->coef);
-      const uint16_t* coef_scale = reinterpret_cast<const uint16_t*>(cb + tp->coef_scale);
-#pragma unroll
-      for (int v = 0; v < PPT; ++v) {
-        const int64_t slot = hN + min(k0 + pk[v], nk - 1);
-        const int8_t* cf = coef + slot * p.r;
-        r.pc0[v] = cf[min(pcol[v], p.r - 1)];
-        r.pc1[v] = cf[min(pcol[v] + 1, p.r - 1)];
-        r.psc[v] = coef_scale[slot];
-      }
-    }
-  };
-  auto load_mu_t = [&](const Raw& r) {
-    if (r.m.e < tp->n_parts) {
-      const uint16_t* mk = reinterpret_cast<const uint16_t*>(r.m.kb + tp->mu_k16);
-      const uint16_t* mv = reinterpret_cast<const uint16_t*>(r.m.kb + tp->mu_v16);
-#pragma unroll
-      for (int u = 0; u < IPT; ++u) {
-        const int c = min(r.idx[u], (it_v[u] ? p.C_v : p.C_k) - 1);
-        const uint16_t* mrow = it_v[u] ? mv + ((int64_t)h * p.C_v + c) * D : mk + ((int64_t)h * p.C_k + c) * D;
-        const uint4* m = reinterpret_cast<const uint4*>(mrow + 16 * it_g[u]);
-        m0[u] = m[0];
-        m1[u] = m[1];
-      }
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int kk = min(r.m.k0 + it_key[u], p.n_loc - 1);
-      const uint16_t* row = it_v[u] ? static_cast<const uint16_t*>(p.v_loc) + (int64_t)h * p.vl_head_stride +
-                                          (int64_t)kk * p.vl_token_stride
-                                    : static_cast<const uint16_t*>(p.k_loc) + (int64_t)h * p.kl_head_stride +
-                                          (int64_t)kk * p.kl_token_stride;
-      const uint4* m = reinterpret_cast<const uint4*>(row + 16 * it_g[u]);
-      m0[u] = m[0];
-      m1[u] = m[1];
-    }
-  };
   const uint32_t magic_v = 0x64006400u;  // kept in a VGPR, the mask in an SGPR (one constant-bus read)
   const uint32_t mask_s = 0x00030003u;
-  auto rebuild = [&](int buf, const Raw& r) {
-    _Float16* base = lds + buf * BUF;
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      uint4 o0, o1;
-      rebuild16(r.cw[u], r.zs[u], m0[u], m1[u], o0, o1, magic_v, mask_s);
-      _Float16* dst = it_v[u] ? base + KT + it_key[u] * VROW + 16 * it_g[u] : base + it_key[u] * KROW + 16 * it_g[u];
-      reinterpret_cast<uint4*>(dst)[0] = o0;
-      reinterpret_cast<uint4*>(dst)[1] = o1;
-    }
-    if constexpr (PS) {
-#pragma unroll
-      for (int v = 0; v < PPT; ++v) {
-        const float sg = (float)__builtin_bit_cast(_Float16, r.psc[v]);
-        const float a = pcol[v] < p.r ? (float)r.pc0[v] : 0.f, b = pcol[v] + 1 < p.r ? (float)r.pc1[v] : 0.f;
-        *reinterpret_cast<h2_t*>(base + pk[v] * KROW + D + ppos[v]) = h2_t{(_Float16)(a * sg), (_Float16)(b * sg)};
-      }
-    }
-  };
-
-  // rebuild of tile t in the multi-part kernel: local rows are converted
-  // from bf16 to fp16 in paired channel order, their PSAC columns are zero
-  auto rebuild_t = [&](int buf, const Raw& r) {
-    if (r.m.e < tp->n_parts) {
-      rebuild(buf, r);
-      return;
-    }
-    _Float16* base = lds + buf * BUF;
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const uint32_t a[4] = {m0[u].x, m0[u].y, m0[u].z, m0[u].w}, b[4] = {m1[u].x, m1[u].y, m1[u].z, m1[u].w};
-      uint32_t w[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const uint32_t x = a[jj >> 1], y = b[jj >> 1];
-        const float lo = __uint_as_float((jj & 1) ? (x & 0xffff0000u) : (x << 16));
-        const float hi = __uint_as_float((jj & 1) ? (y & 0xffff0000u) : (y << 16));
-        w[jj] = as_u32(h2_t{(_Float16)lo, (_Float16)hi});
-      }
-      _Float16* dst = it_v[u] ? base + KT + it_key[u] * VROW + 16 * it_g[u] : base + it_key[u] * KROW + 16 * it_g[u];
-      reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    }
-    if constexpr (PS) {
-#pragma unroll
-      for (int v = 0; v < PPT; ++v) *reinterpret_cast<uint32_t*>(base + pk[v] * KROW + D + ppos[v]) = 0u;
-    }
-  };
 
   float m_run = -INFINITY;  // running max, log2 units
   float l_run = 0.f;        // this lane's share of the sum of probabilities
@@ -488,46 +305,122 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
-  Meta mj{};  // multi-part kernel: the part of tile j
-  if (ntiles > 0) {
-    if constexpr (MULTI) {
-      load_cache_t(tb, ra);
-      load_mu_t(ra);
-      rebuild_t(0, ra);
-      mj = ra.m;
-      load_cache_t(tb + 1, ra);
-    } else {
-      load_cache(kbeg, ra);
-      load_mu(ra);
-      rebuild(0, ra);
-      load_cache(kbeg + BN, ra);
-    }
-  }
-  __syncthreads();
-
   const float sl2 = p.scale_log2;
   const int trow = 4 * hf + ((lane & 15) >> 2);             // transposed read: key row in a 16-key chunk
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // and channel position in a 32-channel block
-  for (int j = 0; j < ntiles; ++j) {
-    const int t0 = MULTI ? mj.k0 : kbeg + j * BN;
-    // end of the keys of this tile's part (multi-part kernel), else of the segment
-    const int tend = MULTI ? mj.tend : kend;
-    if constexpr (MULTI) {
-      load_mu_t(ra);                // centre rows (local tiles: the rows) of tile j+1
-      load_cache_t(tb + j + 2, rb);
-    } else {
-      load_mu(ra);                  // centre rows of tile j+1
-      load_cache(t0 + 2 * BN, rb);  // cache fields of tile j+2
+
+  // The pipelined loop over nt tiles of one part, from key kbeg of that part;
+  // kend ends the keys (masked beyond; loads past it read key kend - 1 again).
+  // LOC: the part is the local chunk (bf16 rows converted to fp16 in paired
+  // channel order, zero PSAC columns) and F is unused.
+  auto tile_loop = [&](const Fields& F, int kbeg, int nt, int kend, auto loc_tag) {
+    constexpr bool LOC = decltype(loc_tag)::value;
+    auto slot_of = [&](int key) { return hN + min(key, kend - 1); };
+    auto load_cache = [&](int t0, Raw& r) {
+      if constexpr (!LOC) {
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+          const int key = min(t0 + it_key[u], kend - 1);
+          const int64_t slot = hN + key;
+          const uint32_t fr = ((uint32_t)key + __umulhi((uint32_t)key, p.divF_lo)) >> p.divF_s;
+          const int tt = (int)fr * p.tpf + ((key - (int)fr * p.F) >> p.log2T);
+          const int g = it_g[u];
+          r.cw[u] = (it_v[u] ? F.codes_v : F.codes_k)[slot * NG + g];
+          r.zs[u] = (it_v[u] ? F.params_v : F.params_k)[(hP + tt) * NG + g];
+          const void* ib = it_v[u] ? F.idx_v : F.idx_k;
+          const int bytes = it_v[u] ? p.idx_v_bytes : p.idx_k_bytes;
+          r.idx[u] = bytes == 1 ? (int)static_cast<const uint8_t*>(ib)[slot] : (int)static_cast<const uint16_t*>(ib)[slot];
+        }
+        if constexpr (PS) {
+          // unconditional loads (columns past the rank are masked at the rebuild),
+          // so that nothing waits for them before the rebuild
+#pragma unroll
+          for (int v = 0; v < PPT; ++v) {
+            const int64_t slot = slot_of(t0 + pk[v]);
+            const int8_t* cf = F.coef + slot * p.r;
+            r.pc0[v] = cf[min(pcol[v], p.r - 1)];
+            r.pc1[v] = cf[min(pcol[v] + 1, p.r - 1)];
+            r.psc[v] = F.coef_scale[slot];
+          }
+        }
+      }
+    };
+    // centre rows of a prefetched tile (local chunk: the rows themselves, of
+    // the tile starting at key t0)
+    auto load_mu = [&](const Raw& r, int t0) {
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) {
+        const uint16_t* row;
+        if constexpr (LOC) {
+          const int kk = min(t0 + it_key[u], kend - 1);
+          row = it_v[u] ? static_cast<const uint16_t*>(p.v_loc) + (int64_t)h * p.vl_head_stride +
+                              (int64_t)kk * p.vl_token_stride
+                        : static_cast<const uint16_t*>(p.k_loc) + (int64_t)h * p.kl_head_stride +
+                              (int64_t)kk * p.kl_token_stride;
+        } else {
+          const int c = min(r.idx[u], (it_v[u] ? p.C_v : p.C_k) - 1);
+          row = it_v[u] ? F.mu_v16 + ((int64_t)h * p.C_v + c) * D : F.mu_k16 + ((int64_t)h * p.C_k + c) * D;
+        }
+        const uint4* m = reinterpret_cast<const uint4*>(row + 16 * it_g[u]);
+        m0[u] = m[0];
+        m1[u] = m[1];
+      }
+    };
+    auto rebuild = [&](int buf, const Raw& r) {
+      _Float16* base = lds + buf * BUF;
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) {
+        uint4 o0, o1;
+        if constexpr (LOC) {
+          // bf16 channel order -> fp16 pairs (channel j, channel j + 8)
+          const uint32_t a[4] = {m0[u].x, m0[u].y, m0[u].z, m0[u].w}, b[4] = {m1[u].x, m1[u].y, m1[u].z, m1[u].w};
+          uint32_t w[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const uint32_t x = a[jj >> 1], y = b[jj >> 1];
+            const float lo = __uint_as_float((jj & 1) ? (x & 0xffff0000u) : (x << 16));
+            const float hi = __uint_as_float((jj & 1) ? (y & 0xffff0000u) : (y << 16));
+            w[jj] = as_u32(h2_t{(_Float16)lo, (_Float16)hi});
+          }
+          o0 = make_uint4(w[0], w[1], w[2], w[3]);
+          o1 = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+          rebuild16(r.cw[u], r.zs[u], m0[u], m1[u], o0, o1, magic_v, mask_s);
+        }
+        _Float16* dst = it_v[u] ? base + KT + it_key[u] * VROW + 16 * it_g[u] : base + it_key[u] * KROW + 16 * it_g[u];
+        reinterpret_cast<uint4*>(dst)[0] = o0;
+        reinterpret_cast<uint4*>(dst)[1] = o1;
+      }
+      if constexpr (PS) {
+#pragma unroll
+        for (int v = 0; v < PPT; ++v) {
+          if constexpr (LOC) {
+            *reinterpret_cast<uint32_t*>(base + pk[v] * KROW + D + ppos[v]) = 0u;
+          } else {
+            const float sg = (float)__builtin_bit_cast(_Float16, r.psc[v]);
+            const float a = pcol[v] < p.r ? (float)r.pc0[v] : 0.f, b = pcol[v] + 1 < p.r ? (float)r.pc1[v] : 0.f;
+            *reinterpret_cast<h2_t*>(base + pk[v] * KROW + D + ppos[v]) = h2_t{(_Float16)(a * sg), (_Float16)(b * sg)};
+          }
+        }
+      }
+    };
+
+    Raw ra, rb;  // tiles j+1 and j+2
+    const int tend = kend;
+    if (nt > 0) {
+      load_cache(kbeg, ra);
+      load_mu(ra, kbeg);
+      rebuild(0, ra);
+      load_cache(kbeg + BN, ra);
     }
+    __syncthreads();
+    for (int j = 0; j < nt; ++j) {
+      const int t0 = kbeg + j * BN;
+      load_mu(ra, t0 + BN);         // centre rows (local chunk: the rows) of tile j+1
+      load_cache(t0 + 2 * BN, rb);  // cache fields of tile j+2
     const _Float16* kt = lds + (j & 1) * BUF;
     const _Float16* vt = kt + KT;
     if (__builtin_amdgcn_readfirstlane(wave_active)) {
-      if constexpr (MULTI && PS) {
-        if (mj.e != cur_e && mj.e < tp->n_parts) {  // entering another epoch (uniform)
-          refresh_uq(mj.kb);
-          cur_e = mj.e;
-        }
-      }
       // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
       f32x16 s[2];
       const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -586,8 +479,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
       // rebuild of the next tile into the other buffer: independent VALU work
       // for the scheduler to place among the P V MFMAs
-      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra);
-      else rebuild((j + 1) & 1, ra);
+      rebuild((j + 1) & 1, ra);
       // ---- O^T += V~^T P^T ----
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -600,12 +492,44 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
           o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
         }
     } else {
-      if constexpr (MULTI) rebuild_t((j + 1) & 1, ra);
-      else rebuild((j + 1) & 1, ra);
+      rebuild((j + 1) & 1, ra);
     }
-    if constexpr (MULTI) mj = ra.m;
-    ra = rb;
-    __syncthreads();
+      ra = rb;
+      __syncthreads();
+    }
+  };
+
+  if constexpr (!MULTI) {
+    tile_loop(Fields{p.idx_k, p.idx_v, p.codes_k, p.codes_v, p.params_k, p.params_v, p.coef, p.coef_scale,
+                     p.mu_k16, p.mu_v16, p.ut16},
+              tb * BN, te - tb, min(p.n_k, te * BN), std::false_type{});
+  } else {
+    // the parts the segment touches, in order (uniform scalar loop); U^T q is
+    // formed for the first compressed part and again at each change of part
+    bool uq = false;
+    for (int e = 0; e < tp->n_parts; ++e) {
+      const CachePart cp = part_at(*tp, e);
+      const int pend = e + 1 < tp->n_parts ? part_at(*tp, e + 1).tile0 : tp->local0;
+      const int a = max(tb, cp.tile0), b = min(te, pend);
+      if (a >= b) continue;
+      const Fields f = fields_of(cp);
+      form_uq(f.ut16);
+      uq = true;
+      tile_loop(f, (a - cp.tile0) * BN, b - a, min(cp.n_k, (b - cp.tile0) * BN), std::false_type{});
+    }
+    const int a = max(tb, tp->local0);
+    if (a < te) {
+      // local tiles have zero PSAC columns: the Q fragment's U^T q (any, or
+      // zero when no compressed part came first) does not enter the scores
+      if (!uq) {
+#pragma unroll
+        for (int ks = NG; ks < NKS; ++ks)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qf[ks][i] = (_Float16)0.f;
+      }
+      const Fields f = fields_of(part_at(*tp, 0));
+      tile_loop(f, (a - tp->local0) * BN, te - a, min(p.n_loc, (te - tp->local0) * BN), std::true_type{});
+    }
   }
 
   if (!wave_active) return;
