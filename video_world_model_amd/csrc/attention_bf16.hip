@@ -37,10 +37,11 @@
 //    blocks cut between workgroups leave partial results that a small combine
 //    kernel merges by log-sum-exp.
 //  * The key axis can run through several parts in one launch (a separate
-//    kernel instantiation, MULTI): compressed caches of successive calibration
-//    epochs, each rebuilt with its own centres and compensated with its own U
-//    (U^T q is recomputed where a segment enters another epoch), then
-//    optionally the current chunk's own bf16 keys and values.
+//    kernel, MULTI): compressed caches of successive calibration epochs, each
+//    rebuilt with its own centres and compensated with its own U, then
+//    optionally the current chunk's own bf16 keys and values.  A segment runs
+//    the same pipelined tile loop once per part it touches, with the part's
+//    fields fixed and U^T q formed for it; the softmax state carries over.
 #include "qwm_internal.h"
 
 #include <algorithm>
@@ -418,82 +419,82 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       const int t0 = kbeg + j * BN;
       load_mu(ra, t0 + BN);         // centre rows (local chunk: the rows) of tile j+1
       load_cache(t0 + 2 * BN, rb);  // cache fields of tile j+2
-    const _Float16* kt = lds + (j & 1) * BUF;
-    const _Float16* vt = kt + KT;
-    if (__builtin_amdgcn_readfirstlane(wave_active)) {
-      // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
-      f32x16 s[2];
-      const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const _Float16* kt = lds + (j & 1) * BUF;
+      const _Float16* vt = kt + KT;
+      if (__builtin_amdgcn_readfirstlane(wave_active)) {
+        // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
+        f32x16 s[2];
+        const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const h8_t a = *reinterpret_cast<const h8_t*>(kt + (32 * mb + l32) * KROW + 16 * ks + 8 * hf);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? zero16 : s[mb], 0, 0, 0);
+          for (int ks = 0; ks < NKS; ++ks) {
+            const h8_t a = *reinterpret_cast<const h8_t*>(kt + (32 * mb + l32) * KROW + 16 * ks + 8 * hf);
+            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? zero16 : s[mb], 0, 0, 0);
+          }
         }
-      }
-      // keep four K~ fragments in flight ahead of the MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // keep four K~ fragments in flight ahead of the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * NKS - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (__builtin_amdgcn_readfirstlane(t0 + BN > tend)) {  // last tile of a part (uniform)
+        for (int i = 0; i < 2 * NKS - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (__builtin_amdgcn_readfirstlane(t0 + BN > tend)) {  // last tile of a part (uniform)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (t0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3) >= tend) s[mb][i] = -INFINITY;
+        }
+        // ---- online softmax, base 2 ----
+        float mx = s[0][0];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+          l_run *= alpha;
+#pragma unroll
+          for (int b = 0; b < NDB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
+          m_run = m_new;
+        }
+        const float moff = -m_run;
+        h8_t pf[4];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (t0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3) >= tend) s[mb][i] = -INFINITY;
+            pf[2 * mb + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, moff));
+        // the sum uses the rounded probabilities that enter P V (exact products, fp32 sum)
+        const h2_t one = h2_t{(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
+        // rebuild of the next tile into the other buffer: independent VALU work
+        // for the scheduler to place among the P V MFMAs
+        rebuild((j + 1) & 1, ra);
+        // ---- O^T += V~^T P^T ----
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int b = 0; b < NDB; ++b) {
+            const _Float16* va = vt + (16 * c + trow) * VROW + 32 * b + tcol;
+            const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va));
+            const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va + 8 * VROW));
+            const h8_t a = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
+          }
+      } else {
+        rebuild((j + 1) & 1, ra);
       }
-      // ---- online softmax, base 2 ----
-      float mx = s[0][0];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < NDB; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
-        m_run = m_new;
-      }
-      const float moff = -m_run;
-      h8_t pf[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          pf[2 * mb + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, moff));
-      // the sum uses the rounded probabilities that enter P V (exact products, fp32 sum)
-      const h2_t one = h2_t{(_Float16)1.f, (_Float16)1.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
-      // rebuild of the next tile into the other buffer: independent VALU work
-      // for the scheduler to place among the P V MFMAs
-      rebuild((j + 1) & 1, ra);
-      // ---- O^T += V~^T P^T ----
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int b = 0; b < NDB; ++b) {
-          const _Float16* va = vt + (16 * c + trow) * VROW + 32 * b + tcol;
-          const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va));
-          const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va + 8 * VROW));
-          const h8_t a = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
-        }
-    } else {
-      rebuild((j + 1) & 1, ra);
-    }
       ra = rb;
       __syncthreads();
     }
