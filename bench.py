@@ -75,7 +75,7 @@ def top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, seed, qwm, torch):
     the rebuilt keys differs from the one under the original keys, for the
     four modes of the method: QVG (nearest centre, no compensation), QSAC
     only, PSAC only, and both (QuantWM); then QuantWM over compensation ranks
-    r in {0, 4, 8, 16}, and QuantWM with the stage-2 score taken on the exact
+    r in {0, 4, 8, 16, 32}, and QuantWM with the stage-2 score taken on the exact
     INT2 error in the diagonal and in the full quadratic form of Eq. 7.  Each
     setting calibrates and fills a cache of its own; the append of the three
     stage-2 scores is timed (HIP events, mean of three appends after one
@@ -86,7 +86,7 @@ def top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, seed, qwm, torch):
     dense = qwm.dense_top1(cfg, q, k)
     modes = {"qvg": (qwm.QVG_MODE, 0), "qsac_only": (0, 0), "psac_only": (qwm.QVG_MODE, w.rank),
              "quantwm": (0, w.rank)}
-    modes.update({"quantwm_r%d" % r: (0, r) for r in (4, 16) if r != w.rank})
+    modes.update({"quantwm_r%d" % r: (0, r) for r in (4, 16, 32) if r != w.rank})
     modes.update({"quantwm_exact": (qwm.EXACT_ERROR, w.rank), "quantwm_full": (qwm.FULL_QUADRATIC, w.rank)})
     timed = ("quantwm", "quantwm_exact", "quantwm_full")
     # logit MSE on the first 64 queries of every head: mean of (l - l~)^2 over

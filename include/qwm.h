@@ -91,7 +91,7 @@ typedef struct qwm_config {
   int32_t group_channels;   /* residual group width; must be 16 */
   int32_t group_tokens;     /* T in {1,2,4,8,16,32}: tokens sharing one (zero, scale) */
   int32_t top_candidates;   /* K_c in [0, 8]: QSAC stage-1 candidates (0: nearest) */
-  int32_t rank;             /* r in [0, 16]: PSAC principal directions */
+  int32_t rank;             /* r in [0, 32] (and <= d): PSAC principal directions */
   int32_t io_dtype;         /* QWM_BF16 or QWM_F32 for activations and centres */
   uint32_t flags;           /* QWM_UNIFORM_SENS | QWM_NO_RANGE_TERM | QWM_EXACT_ERROR |
                                QWM_FULL_QUADRATIC */
@@ -112,7 +112,8 @@ typedef struct qwm_strides {
  *   sens   [H][d]       fp32 s = diag(M), the Query second moment's diagonal
  *   u      [H][d][r]    fp32 top-r eigenvectors of M (columns)
  *   derived, filled by qwm_calib_import / qwm_calibrate:
- *   u64    [H][d][r]    fp64 copy of u (exact)
+ *   u64    [H][d][RP]   fp64 copy of u (exact), rows padded with zeros to
+ *                       RP = 8, 16 or 32 columns (the smallest >= r)
  *   sgroup [H][d/16]    fp64 S_g = sum of sens over group g
  *   norm_kw [H][C_K]    fp32 ||mu||_s^2 / 2 (sensitivity-weighted)
  *   norm_k  [H][C_K]    fp32 ||mu||^2 / 2
@@ -122,7 +123,8 @@ typedef struct qwm_strides {
  *                       each 16-channel group, position 2j holds channel j and
  *                       position 2j+1 channel j+8 (j = 0..7)
  *   mu_v16 [H][C_V][d]  the same for mu_v
- *   ut16   [H][16][d]   fp16 U^T in the same channel order; rows >= r are zero
+ *   ut16   [H][UR][d]   fp16 U^T in the same channel order, UR = 16 (r <= 16)
+ *                       or 32 rows; rows >= r are zero
  *   moment [H][d][d]    fp64 full Query second moment M (QWM_FULL_QUADRATIC
  *                       only, else 0 bytes; last in the block, written by
  *                       qwm_calib_import_moment and left alone by

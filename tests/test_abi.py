@@ -46,7 +46,7 @@ def cfg_of(w, **kw):
     ("group_tokens", 12, qwm.ERR_UNSUPPORTED),
     ("c_k", 1024, qwm.ERR_UNSUPPORTED),
     ("c_k", 0, qwm.ERR_INVALID_ARG),
-    ("rank", 17, qwm.ERR_UNSUPPORTED),
+    ("rank", 33, qwm.ERR_UNSUPPORTED),
     ("top_k", 9, qwm.ERR_UNSUPPORTED),
     ("heads", 0, qwm.ERR_INVALID_ARG),
     ("flags", 16, qwm.ERR_INVALID_ARG),

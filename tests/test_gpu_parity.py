@@ -110,6 +110,7 @@ SMALL = workloads.scaled(W["matrix_game"], heads=2, frames=2)
     ("rank0", dict(rank=0)),
     ("rank16", dict(rank=16)),
     ("rank5", dict(rank=5)),
+    ("rank20", dict(rank=20)),
     ("T1", dict(group_tokens=1)),
     ("T4", dict(group_tokens=4)),
     ("T32", dict(group_tokens=32)),
@@ -125,6 +126,40 @@ SMALL = workloads.scaled(W["matrix_game"], heads=2, frames=2)
 ])
 def test_parity_variants(label, ov):
     run_case(SMALL, ov, iters=3)
+
+
+def test_parity_rank32_logits_and_top1():
+    """r = 32: two PSAC k-steps in both attention kernels (softmax, logits and
+    top-1 exports) and the two-pass projection of the append."""
+    run_case(SMALL, dict(rank=32), iters=3, logits=True)
+
+
+def test_parity_rank32_f32_d64():
+    """r = 32 with fp32 activations and head_dim 64 (the generic kernel)."""
+    run_case(W["tiny"], dict(rank=32), iters=10, logits=True)
+
+
+def test_local_chunk_rank32():
+    """The multi-part kernel with two PSAC k-steps: cache + local chunk."""
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=2)
+    cfg = P.cfg_of(w, rank=32)
+    say("case local_chunk rank32")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=3)
+    cache, _ = P.build_cache(cfg, cal, data["k"], data["v"])
+    gpu = P.gpu_fields(cache, cache.n_k)
+    stats = P.Stats()
+    outs = [(P.check_keys_head(cfg, data["k"][h], cal, h, gpu, stats),
+             P.check_values_head(cfg, data["v"][h], cal, h, gpu, stats)) for h in range(cfg.heads)]
+    k_loc = np.stack([workloads.kv_frames(w, h, "k", w.frames, w.frames + 1)[:300] for h in range(cfg.heads)])
+    v_loc = np.stack([workloads.kv_frames(w, h, "v", w.frames, w.frames + 1)[:300] for h in range(cfg.heads)])
+    q = P.to_dev(data["q"], cfg)
+    o, lse = qwm.attention_local(cache, q, P.to_dev(k_loc, cfg), P.to_dev(v_loc, cfg))
+    wo, wl = check_local(cfg, cal, outs, data["q"], k_loc, v_loc, o.float().cpu().numpy(), lse.cpu().numpy(),
+                         range(cfg.heads))
+    say("  local chunk r=32: %.3g %.3g" % (wo, wl))
+    assert wo <= 1.0 and wl <= 1.0
 
 
 @pytest.mark.parametrize("flags", [4, 8])

@@ -883,76 +883,90 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   const int T = p.T;
   const int tile = frame * p.tpf + pos / T;
   const int64_t slot = (int64_t)h * p.Ncap + tok;
-  double cacc[R > 0 ? R : 1];
-#pragma unroll
-  for (int i = 0; i < (R > 0 ? R : 1); ++i) cacc[i] = 0.0;
+  // PSAC accumulates c = U^T e in passes of at most 16 columns (two passes at
+  // R = 32: the second recomputes the residual codes and stores nothing, so
+  // that the fp64 accumulators and U rows of one pass fit in registers)
+  constexpr int RC = R > 16 ? 16 : (R > 0 ? R : 1);  // columns per pass
+  constexpr int NPASS = R > 16 ? 2 : 1;
+  float c32[R > 0 ? R : 1];
   const double* U = u_lds;
 
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    double cacc[RC];
+#pragma unroll
+    for (int i = 0; i < RC; ++i) cacc[i] = 0.0;
 #pragma unroll 1
-  for (int g = 0; g < NG; ++g) {
-    float k[16], m[16];
-    load_k16(g, k);
-    mu_row16(chosen, g, m);
-    float rho[16];
-    rho[0] = k[0] - m[0];
-    float lo = rho[0], hi = rho[0];
+    for (int g = 0; g < NG; ++g) {
+      float k[16], m[16];
+      load_k16(g, k);
+      mu_row16(chosen, g, m);
+      float rho[16];
+      rho[0] = k[0] - m[0];
+      float lo = rho[0], hi = rho[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) {
-      rho[j] = k[j] - m[j];
-      lo = fminf(lo, rho[j]);
-      hi = fmaxf(hi, rho[j]);
-    }
-    if (!valid) { lo = INFINITY; hi = -INFINITY; }
-    // min / max over the T lanes of the tile (T | 32, tiles lane-aligned)
-    if (T > 1) { lo = fminf(lo, dpp_f<0xB1>(lo)); hi = fmaxf(hi, dpp_f<0xB1>(hi)); }    // lane ^ 1
-    if (T > 2) { lo = fminf(lo, dpp_f<0x4E>(lo)); hi = fmaxf(hi, dpp_f<0x4E>(hi)); }    // lane ^ 2
-    if (T > 4) { lo = fminf(lo, dpp_f<0x141>(lo)); hi = fmaxf(hi, dpp_f<0x141>(hi)); }  // 7 - lane in 8
-    if (T > 8) { lo = fminf(lo, dpp_f<0x140>(lo)); hi = fmaxf(hi, dpp_f<0x140>(hi)); }  // 15 - lane in 16
-    if (T > 16) { lo = fminf(lo, __shfl_xor(lo, 16)); hi = fmaxf(hi, __shfl_xor(hi, 16)); }
-    const uint16_t zb = to_half_bits(lo);
-    const uint16_t sb = to_half_bits((hi - lo) / 3.0f);
-    const float zf = half_bits_to_float(zb);
-    const float sf = half_bits_to_float(sb);
-    // a zero scale codes everything as 0 (every finite residual is below +inf)
-    const bool zs = sf == 0.f;
-    const float t1 = zs ? INFINITY : zf + 0.5f * sf;
-    const float t2 = zs ? INFINITY : zf + 1.5f * sf;
-    const float t3 = zs ? INFINITY : zf + 2.5f * sf;
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
-      w |= code << (2 * j);
-    }
-    if constexpr (KEY && R > 0) {
-      // c += U^T e over the group's 16 channels, with the next U row read
-      // while this row's FMAs run: the empty asm statements (no instruction)
-      // keep the rows in order, so at most two rows are live
-      const double* ug = U + 16 * g * R;
-      double ucur[R], unxt[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) ucur[i] = ug[i];
+      for (int j = 1; j < 16; ++j) {
+        rho[j] = k[j] - m[j];
+        lo = fminf(lo, rho[j]);
+        hi = fmaxf(hi, rho[j]);
+      }
+      if (!valid) { lo = INFINITY; hi = -INFINITY; }
+      // min / max over the T lanes of the tile (T | 32, tiles lane-aligned)
+      if (T > 1) { lo = fminf(lo, dpp_f<0xB1>(lo)); hi = fmaxf(hi, dpp_f<0xB1>(hi)); }    // lane ^ 1
+      if (T > 2) { lo = fminf(lo, dpp_f<0x4E>(lo)); hi = fmaxf(hi, dpp_f<0x4E>(hi)); }    // lane ^ 2
+      if (T > 4) { lo = fminf(lo, dpp_f<0x141>(lo)); hi = fmaxf(hi, dpp_f<0x141>(hi)); }  // 7 - lane in 8
+      if (T > 8) { lo = fminf(lo, dpp_f<0x140>(lo)); hi = fmaxf(hi, dpp_f<0x140>(hi)); }  // 15 - lane in 16
+      if (T > 16) { lo = fminf(lo, __shfl_xor(lo, 16)); hi = fmaxf(hi, __shfl_xor(hi, 16)); }
+      const uint16_t zb = to_half_bits(lo);
+      const uint16_t sb = to_half_bits((hi - lo) / 3.0f);
+      const float zf = half_bits_to_float(zb);
+      const float sf = half_bits_to_float(sb);
+      // a zero scale codes everything as 0 (every finite residual is below +inf)
+      const bool zs = sf == 0.f;
+      const float t1 = zs ? INFINITY : zf + 0.5f * sf;
+      const float t2 = zs ? INFINITY : zf + 1.5f * sf;
+      const float t3 = zs ? INFINITY : zf + 2.5f * sf;
+      uint32_t w = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (j + 1 < 16) {
+        const uint32_t code = (uint32_t)(rho[j] >= t1) + (uint32_t)(rho[j] >= t2) + (uint32_t)(rho[j] >= t3);
+        w |= code << (2 * j);
+      }
+      if constexpr (KEY && R > 0) {
+        // c += U^T e over the group's 16 channels (this pass's columns), with
+        // the next U row read while this row's FMAs run: the empty asm
+        // statements (no instruction) keep the rows in order, so at most two
+        // rows are live
+        const double* ug = U + 16 * g * R + 16 * pass;
+        double ucur[RC], unxt[RC];
 #pragma unroll
-          for (int i = 0; i < R; ++i) unxt[i] = ug[(j + 1) * R + i];
+        for (int i = 0; i < RC; ++i) ucur[i] = ug[i];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (j + 1 < 16) {
+#pragma unroll
+            for (int i = 0; i < RC; ++i) unxt[i] = ug[(j + 1) * R + i];
+          }
+          const float rhat = fmaf((float)((w >> (2 * j)) & 3u), sf, zf);
+          const double e = ((double)k[j] - (double)m[j]) - (double)rhat;
+#pragma unroll
+          for (int i = 0; i < RC; ++i) cacc[i] = fma(ucur[i], e, cacc[i]);
+#pragma unroll
+          for (int i = 0; i < RC; ++i) {
+            asm volatile("" : "+v"(cacc[i]));
+            ucur[i] = unxt[i];
+          }
+          asm volatile("" ::: "memory");
         }
-        const float rhat = fmaf((float)((w >> (2 * j)) & 3u), sf, zf);
-        const double e = ((double)k[j] - (double)m[j]) - (double)rhat;
-#pragma unroll
-        for (int i = 0; i < R; ++i) cacc[i] = fma(ucur[i], e, cacc[i]);
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          asm volatile("" : "+v"(cacc[i]));
-          ucur[i] = unxt[i];
-        }
-        asm volatile("" ::: "memory");
+      }
+      if (pass == 0 && valid) {
+        p.codes[slot * NG + g] = w;
+        if ((pos % T) == 0) p.params[((int64_t)h * p.Pcap + tile) * NG + g] = (uint32_t)zb | ((uint32_t)sb << 16);
       }
     }
-    if (valid) {
-      p.codes[slot * NG + g] = w;
-      if ((pos % T) == 0) p.params[((int64_t)h * p.Pcap + tile) * NG + g] = (uint32_t)zb | ((uint32_t)sb << 16);
+    if constexpr (KEY && R > 0) {
+#pragma unroll
+      for (int i = 0; i < RC; ++i) c32[RC * pass + i] = (float)cacc[i];
     }
   }
 
@@ -962,13 +976,10 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
 
   if constexpr (KEY && R > 0) {
     const int r = p.r;
-    float c32[R];
     float a = 0.f;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      c32[i] = (float)cacc[i];
+    for (int i = 0; i < R; ++i)
       if (i < r) a = fmaxf(a, fabsf(c32[i]));
-    }
     const uint16_t sgb = to_half_bits(a / 127.0f);
     const float sg = half_bits_to_float(sgb);
     int8_t n[R];
@@ -985,6 +996,17 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
         pk.x = (uint32_t)(uint8_t)n[0] | ((uint32_t)(uint8_t)n[1] << 8) | ((uint32_t)(uint8_t)n[2] << 16) | ((uint32_t)(uint8_t)n[3] << 24);
         pk.y = (uint32_t)(uint8_t)n[4] | ((uint32_t)(uint8_t)n[5] << 8) | ((uint32_t)(uint8_t)n[6] << 16) | ((uint32_t)(uint8_t)n[7] << 24);
         *reinterpret_cast<uint2*>(dst) = pk;
+      } else if constexpr (R % 16 == 0) {
+        // whole rows of 16-byte words (the row of token t starts at 16 R t / 16)
+#pragma unroll
+        for (int q = 0; q < R / 16; ++q) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            wv[b] = (uint32_t)(uint8_t)n[16 * q + 4 * b] | ((uint32_t)(uint8_t)n[16 * q + 4 * b + 1] << 8) |
+                    ((uint32_t)(uint8_t)n[16 * q + 4 * b + 2] << 16) | ((uint32_t)(uint8_t)n[16 * q + 4 * b + 3] << 24);
+          reinterpret_cast<uint4*>(dst)[q] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < R; ++i) dst[i] = n[i];
@@ -1041,20 +1063,23 @@ hipError_t launch_kv(const AppendParams& pk, const AppendParams& pv, int heads, 
 template <int D, bool F32IO>
 inline hipError_t dispatch_kv_d(const AppendParams& pk, const AppendParams& pv, int heads, hipStream_t stream) {
   const bool argmin = !pk.use_range || pk.Kc <= 1;
-  const int rb = pk.r == 0 ? 0 : (pk.r <= 8 ? 8 : 16);
+  const int rb = pk.rp;
   if (argmin) {
     if (rb == 0) return launch_kv<D, F32IO, 1, 0>(pk, pv, heads, stream);
     if (rb == 8) return launch_kv<D, F32IO, 1, 8>(pk, pv, heads, stream);
-    return launch_kv<D, F32IO, 1, 16>(pk, pv, heads, stream);
+    if (rb == 16) return launch_kv<D, F32IO, 1, 16>(pk, pv, heads, stream);
+    return launch_kv<D, F32IO, 1, 32>(pk, pv, heads, stream);
   }
   if (pk.Kc <= 4) {
     if (rb == 0) return launch_kv<D, F32IO, 4, 0>(pk, pv, heads, stream);
     if (rb == 8) return launch_kv<D, F32IO, 4, 8>(pk, pv, heads, stream);
-    return launch_kv<D, F32IO, 4, 16>(pk, pv, heads, stream);
+    if (rb == 16) return launch_kv<D, F32IO, 4, 16>(pk, pv, heads, stream);
+    return launch_kv<D, F32IO, 4, 32>(pk, pv, heads, stream);
   }
   if (rb == 0) return launch_kv<D, F32IO, 8, 0>(pk, pv, heads, stream);
   if (rb == 8) return launch_kv<D, F32IO, 8, 8>(pk, pv, heads, stream);
-  return launch_kv<D, F32IO, 8, 16>(pk, pv, heads, stream);
+  if (rb == 16) return launch_kv<D, F32IO, 8, 16>(pk, pv, heads, stream);
+  return launch_kv<D, F32IO, 8, 32>(pk, pv, heads, stream);
 }
 
 template <int D, bool F32IO, bool KEY, int KC, int R, int NW>
@@ -1080,20 +1105,23 @@ template <int D, bool F32IO>
 inline hipError_t dispatch_d(const AppendParams& p, int heads, bool key, hipStream_t stream) {
   if (!key) return launch_one<D, F32IO, false, 1, 0>(p, heads, stream);
   const bool argmin = !p.use_range || p.Kc <= 1;
-  const int rb = p.r == 0 ? 0 : (p.r <= 8 ? 8 : 16);
+  const int rb = p.rp;
   if (argmin) {
     if (rb == 0) return launch_one<D, F32IO, true, 1, 0>(p, heads, stream);
     if (rb == 8) return launch_one<D, F32IO, true, 1, 8>(p, heads, stream);
-    return launch_one<D, F32IO, true, 1, 16>(p, heads, stream);
+    if (rb == 16) return launch_one<D, F32IO, true, 1, 16>(p, heads, stream);
+    return launch_one<D, F32IO, true, 1, 32>(p, heads, stream);
   }
   if (p.Kc <= 4) {
     if (rb == 0) return launch_one<D, F32IO, true, 4, 0>(p, heads, stream);
     if (rb == 8) return launch_one<D, F32IO, true, 4, 8>(p, heads, stream);
-    return launch_one<D, F32IO, true, 4, 16>(p, heads, stream);
+    if (rb == 16) return launch_one<D, F32IO, true, 4, 16>(p, heads, stream);
+    return launch_one<D, F32IO, true, 4, 32>(p, heads, stream);
   }
   if (rb == 0) return launch_one<D, F32IO, true, 8, 0>(p, heads, stream);
   if (rb == 8) return launch_one<D, F32IO, true, 8, 8>(p, heads, stream);
-  return launch_one<D, F32IO, true, 8, 16>(p, heads, stream);
+  if (rb == 16) return launch_one<D, F32IO, true, 8, 16>(p, heads, stream);
+  return launch_one<D, F32IO, true, 8, 32>(p, heads, stream);
 }
 
 }  // namespace append_detail

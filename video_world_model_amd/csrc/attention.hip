@@ -8,12 +8,13 @@
 //
 // Design.  A workgroup of 4 waves owns 128 queries of one head (32 per wave)
 // and one key range (split-KV).  Per 64-key tile the workgroup rebuilds
-//   K~ [64][d + 16] fp16 in LDS: mu_K[idx] + (z + code s) in fp32, rounded
-//        once to fp16; the 16 extra columns hold c_hat = coef * sigma,
+//   K~ [64][d + 16 n] fp16 in LDS: mu_K[idx] + (z + code s) in fp32, rounded
+//        once to fp16; the 16 n extra columns (n = 1 for r <= 16, 2 for
+//        r <= 32) hold c_hat = coef * sigma,
 //   V~^T [d][64] fp16 in LDS, keys permuted inside each 16-key chunk so that
 //        the P^T operand can be taken straight from the S^T accumulators.
 // Each wave computes S^T = K~ [Q | U^T q]^T with v_mfma_f32_32x32x16_f16
-// (lane = query, 16 keys per 32-key block), so PSAC costs 16 extra
+// (lane = query, 16 keys per 32-key block), so PSAC costs 16 n extra
 // contraction columns instead of per-element work: q.(k_hat + U c_hat) =
 // q.k_hat + (U^T q).c_hat.  Online softmax in base 2, then O^T += V~^T P^T.
 #include "qwm_internal.h"
@@ -57,9 +58,10 @@ __device__ __forceinline__ int load_idx(const void* base, int bytes, int64_t i) 
 // position of key k (0..15) of a 16-key chunk in the V~^T LDS rows
 __device__ __forceinline__ int vperm(int k) { return 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3); }
 
-template <int D, bool F32IO, int MODE>
+// NPS: 16-column PSAC k-steps (1 for r <= 16, 2 for r <= 32)
+template <int D, bool F32IO, int MODE, int NPS>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
-  constexpr int DA = D + 16;       // contraction incl. the PSAC columns
+  constexpr int DA = D + 16 * NPS; // contraction incl. the PSAC columns
   constexpr int KROW = DA + 8;     // fp16 pitch of K~ rows
   constexpr int VROW = BN + 8;     // fp16 pitch of V~^T rows
   constexpr int NKS = DA / 16;     // MFMA k-steps for S
@@ -84,16 +86,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 
   // ---- Q fragment [q | U^T q] as fp16, lane = query, half hf holds k-slots 8hf..8hf+7 ----
   half8 qf[NKS];
-  half8 qlo[F32IO ? NKS - 1 : 1];  // fp32 queries: the fp16 remainder q - fp16(q)
+  half8 qlo[F32IO ? NG : 1];  // fp32 queries: the fp16 remainder q - fp16(q)
   {
     const void* qrow = F32IO
         ? static_cast<const void*>(static_cast<const float*>(p.q) + (int64_t)h * p.q_head_stride)
         : static_cast<const void*>(static_cast<const uint16_t*>(p.q) + (int64_t)h * p.q_head_stride);
     const int64_t qoff = (int64_t)(qvalid ? qi : 0) * p.q_token_stride;
     const float* U = p.u + (int64_t)h * D * p.r;
-    float uq[16];
+    float uq[16 * NPS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) uq[i] = 0.f;
+    for (int i = 0; i < 16 * NPS; ++i) uq[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int c0 = 16 * ks + 8 * hf;
@@ -105,14 +107,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
         qf[ks][i] = (_Float16)v[i];
         if constexpr (F32IO) qlo[ks][i] = (_Float16)(v[i] - (float)qf[ks][i]);
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
+        for (int rr = 0; rr < 16 * NPS; ++rr)
           if (rr < p.r) uq[rr] = fmaf(U[(c0 + i) * p.r + rr], v[i], uq[rr]);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) uq[i] += __shfl_xor(uq[i], 32);
+    for (int i = 0; i < 16 * NPS; ++i) uq[i] += __shfl_xor(uq[i], 32);
+    // PSAC k-step s: half hf holds directions 16s + 8hf .. 16s + 8hf + 7
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qf[NKS - 1][i] = (_Float16)(hf ? uq[8 + i] : uq[i]);
+    for (int s2 = 0; s2 < NPS; ++s2)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[NG + s2][i] = (_Float16)(hf ? uq[16 * s2 + 8 + i] : uq[16 * s2 + i]);
   }
 
   const int kbeg = split * p.keys_per_split;
@@ -181,22 +186,26 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
         }
       }
       if (qq == 0) {
-        half8 c0, c1;
         float sg = 0.f;
         if (kv && p.r > 0) sg = h2f(p.coef_scale[slot]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          c0[i] = (_Float16)((kv && i < p.r) ? (float)p.coef[slot * p.r + i] * sg : 0.f);
-          c1[i] = (_Float16)((kv && 8 + i < p.r) ? (float)p.coef[slot * p.r + 8 + i] * sg : 0.f);
-        }
-        *reinterpret_cast<half8*>(&kt[kk * KROW + D]) = c0;
-        *reinterpret_cast<half8*>(&kt[kk * KROW + D + 8]) = c1;
-        if constexpr (F32IO) {
-          half8 zz;
+        for (int s2 = 0; s2 < NPS; ++s2) {
+          half8 c0, c1;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) zz[i] = (_Float16)0.f;
-          *reinterpret_cast<half8*>(&kt_lo[kk * KROW + D]) = zz;
-          *reinterpret_cast<half8*>(&kt_lo[kk * KROW + D + 8]) = zz;
+          for (int i = 0; i < 8; ++i) {
+            const int d0 = 16 * s2 + i, d1 = 16 * s2 + 8 + i;
+            c0[i] = (_Float16)((kv && d0 < p.r) ? (float)p.coef[slot * p.r + d0] * sg : 0.f);
+            c1[i] = (_Float16)((kv && d1 < p.r) ? (float)p.coef[slot * p.r + d1] * sg : 0.f);
+          }
+          *reinterpret_cast<half8*>(&kt[kk * KROW + D + 16 * s2]) = c0;
+          *reinterpret_cast<half8*>(&kt[kk * KROW + D + 16 * s2 + 8]) = c1;
+          if constexpr (F32IO) {
+            half8 zz;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) zz[i] = (_Float16)0.f;
+            *reinterpret_cast<half8*>(&kt_lo[kk * KROW + D + 16 * s2]) = zz;
+            *reinterpret_cast<half8*>(&kt_lo[kk * KROW + D + 16 * s2 + 8]) = zz;
+          }
         }
       }
       if constexpr (MODE != MODE_TOP1) {
@@ -244,7 +253,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
         const half8 a = *reinterpret_cast<const half8*>(&kt[(32 * mb + l32) * KROW + 16 * ks + 8 * hf]);
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], s[mb], 0, 0, 0);
         if constexpr (F32IO) {
-          if (ks < NKS - 1) {
+          if (ks < NG) {
             s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qlo[ks], s[mb], 0, 0, 0);
             const half8 al = *reinterpret_cast<const half8*>(&kt_lo[(32 * mb + l32) * KROW + 16 * ks + 8 * hf]);
             s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qf[ks], s[mb], 0, 0, 0);
@@ -384,24 +393,29 @@ __global__ __launch_bounds__(D) void combine_kernel(AttnParams p, int heads) {
   if (d == 0 && p.lse) p.lse[(int64_t)h * p.n_q + qi] = tot > 0.f ? top + __logf(tot) : -INFINITY;
 }
 
-template <int D, bool F32IO>
-hipError_t launch_d(const AttnParams& p, int heads, hipStream_t stream) {
+template <int D, bool F32IO, int NPS>
+hipError_t launch_dn(const AttnParams& p, int heads, hipStream_t stream) {
   dim3 grid((p.n_q + BM - 1) / BM, heads, p.splits);
   if (p.ev_begin) {
     const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(p.ev_begin), stream);
     if (er != hipSuccess) return er;
   }
   if (p.top1) {
-    hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_TOP1>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_TOP1, NPS>), grid, dim3(256), 0, stream, p);
   } else if (p.logits) {
-    hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_LOGITS>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_LOGITS, NPS>), grid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_ATTN>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<D, F32IO, MODE_ATTN, NPS>), grid, dim3(256), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || p.splits == 1 || p.top1 || p.logits) return e;
   return launch_combine(p, heads, D, F32IO, stream);
+}
+
+template <int D, bool F32IO>
+hipError_t launch_d(const AttnParams& p, int heads, hipStream_t stream) {
+  return p.r > 16 ? launch_dn<D, F32IO, 2>(p, heads, stream) : launch_dn<D, F32IO, 1>(p, heads, stream);
 }
 
 // Top-1 over original keys: one thread per (head, query), fp32 dot products.

@@ -26,8 +26,9 @@
 //  * V~ is stored row-major like K~ and read with ds_read_b64_tr_b16, which
 //    gives each lane four consecutive keys of one channel: the A operand of
 //    O^T += V~^T P^T, without a transposing store.
-//  * PSAC as 16 extra contraction columns: q.(k_hat + U c_hat) = q.k_hat +
-//    (U^T q).c_hat, with U^T q computed once per workgroup on the MFMA unit.
+//  * PSAC as 16 (r <= 16) or 32 (r <= 32) extra contraction columns:
+//    q.(k_hat + U c_hat) = q.k_hat + (U^T q).c_hat, with U^T q computed once
+//    per workgroup on the MFMA unit.
 //  * Online softmax in base 2 with a lazy running max: it only moves when a
 //    tile's maximum exceeds it by more than 8, so probabilities stay below 2^8
 //    and most tiles skip the rescaling of the accumulators.
@@ -92,8 +93,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // Position of PSAC column k in the K~ rows (and of U^T q in the Q fragment):
 // the MFMA that computes U^T q leaves columns 4hf..4hf+3 and 8+4hf..8+4hf+3 in
-// lane half hf.
+// lane half hf (within each 16-column k-step; the map swaps bits 2 and 3, so
+// it is its own inverse).
 __device__ __forceinline__ int psac_col(int k) { return 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3); }
+
+// fp16 pitch of the K~ rows in LDS: d channels, 16 or 32 PSAC columns, 8 pad
+template <int D, int NPS>
+constexpr int kKRow = D + 8 + 16 * (NPS > 1 ? NPS : 1);
 
 // One pair of rebuilt values, each rounded to fp16 once:
 //   (mu.lo + (c.lo s + z), mu.hi + (c.hi s + z))
@@ -167,23 +173,25 @@ static_assert(kMaxParts == 16, "part_at covers 16 parts");
 // then the local chunk).  The segment then runs the pipelined tile loop once
 // per part it touches, with that part's fields fixed (the loop restarts at a
 // part boundary), and forms U^T q again on entering another epoch.
-template <int D, bool PS, int NW, bool MULTI>
+template <int D, int NPS, int NW, bool MULTI>
 __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, const PartTable* tp,
                                                _Float16* lds, int pair, int tb, int te, int slot) {
   // tp: read by the multi-part instantiation only (null in the other)
   constexpr int NT = 64 * NW;             // threads per workgroup
   constexpr int NG = D / 16;
-  constexpr int NKS = NG + (PS ? 1 : 0);  // MFMA k-steps of S (last: PSAC columns)
-  constexpr int KROW = D + 24;            // fp16 pitch of K~ rows: d channels, 16 PSAC columns, 8 pad
+  constexpr bool PS = NPS > 0;           // PSAC compensation (r > 0)
+  constexpr int NPX = PS ? NPS : 1;
+  constexpr int NKS = NG + NPS;           // MFMA k-steps of S (the last NPS: PSAC columns)
+  constexpr int KROW = kKRow<D, NPS>;     // fp16 pitch of K~ rows: d channels, 16 NPX PSAC columns, 8 pad
   constexpr int VROW = D + 32;            // fp16 pitch of V~ rows
   constexpr int KT = BN * KROW;
   constexpr int BUF = KT + BN * VROW;
   constexpr int NDB = D / 32;             // 32-row blocks of O^T
   constexpr int ITEMS = BN * NG;          // (key, group) rebuild items per tensor
   constexpr int IPT = 2 * ITEMS / NT;     // items per thread
-  constexpr int PPT = BN * 8 / NT;        // PSAC column pairs per thread
+  constexpr int PPT = BN * 8 * NPX / NT;  // PSAC column pairs per thread
   static_assert(IPT * NT == 2 * ITEMS && IPT >= 1 && IPT <= 4, "rebuild split");
-  static_assert(PPT * NT == BN * 8 && PPT >= 1, "PSAC split");
+  static_assert(PPT * NT == BN * 8 * NPX && PPT >= 1, "PSAC split");
 
   const int qb = pair % gr.n_qb;
   const int h = pair / gr.n_qb;
@@ -241,23 +249,27 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
                     bf_to_h(a.y & 0xffffu), bf_to_h(b.y & 0xffffu), bf_to_h(a.y >> 16), bf_to_h(b.y >> 16)};
     }
   }
-  // U^T q of one calibration into the PSAC k-step of the Q fragment
+  // U^T q of one calibration into the PSAC k-steps of the Q fragment: rows
+  // 0..16 NPS - 1 of the 32-row MFMA are the directions (U^T has 16 NPS rows
+  // per head), accumulator values 8s..8s+7 fill PSAC k-step s
   auto form_uq = [&](const uint16_t* ut16) {
     if constexpr (PS) {
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      const uint16_t* ut = ut16 + (int64_t)h * 16 * D;
+      const uint16_t* ut = ut16 + (int64_t)h * 16 * NPS * D;
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         h8_t a;
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[i] = (_Float16)0.f;
-        if (l32 < 16) a = *reinterpret_cast<const h8_t*>(ut + l32 * D + 16 * ks + 8 * hf);
+        if (l32 < 16 * NPS) a = *reinterpret_cast<const h8_t*>(ut + l32 * D + 16 * ks + 8 * hf);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[NG][i] = (_Float16)acc[i];
+      for (int s2 = 0; s2 < NPS; ++s2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[NG + s2][i] = (_Float16)acc[8 * s2 + i];
     }
   };
   if constexpr (!MULTI) form_uq(p.ut16);
@@ -277,9 +289,9 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 #pragma unroll
   for (int v = 0; v < PPT; ++v) {
     const int it = tid + v * NT;
-    pk[v] = it >> 3;
-    ppos[v] = 2 * (it & 7);
-    pcol[v] = psac_col(ppos[v]);
+    pk[v] = it / (8 * NPX);
+    ppos[v] = 2 * (it % (8 * NPX));
+    pcol[v] = 16 * (ppos[v] >> 4) + psac_col(ppos[v] & 15);
   }
 
   const int64_t hN = (int64_t)h * p.Ncap;
@@ -572,15 +584,15 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 
 // MULTI: the key axis runs through the parts of the table (a separate
 // kernel, so the single-cache one carries none of their code or arguments)
-template <int D, bool PS, int NW, bool MULTI>
+template <int D, int NPS, int NW, bool MULTI>
 __device__ __forceinline__ void attn_bf16_body(const AttnParams& p, const Grid& gr, const PartTable* tbl) {
-  constexpr int BUF = BN * (D + 24) + BN * (D + 32);
+  constexpr int BUF = BN * kKRow<D, NPS> + BN * (D + 32);
   __shared__ __align__(16) _Float16 lds[2 * BUF];
   const int bid = blockIdx.x;
   const int w = (bid & 7) * gr.per_xcd + (bid >> 3);
   if (w >= gr.G) return;
   if (gr.ntiles == 0) {  // no keys at all: every pair writes zeros and lse = -inf
-    attend_segment<D, PS, NW, MULTI>(p, gr, tbl, lds, w, 0, 0, -1);
+    attend_segment<D, NPS, NW, MULTI>(p, gr, tbl, lds, w, 0, 0, -1);
     return;
   }
   const long long u0 = (long long)w * gr.units / gr.G;
@@ -592,21 +604,21 @@ __device__ __forceinline__ void attn_bf16_body(const AttnParams& p, const Grid& 
     const int tb = (int)(u % gr.ntiles);
     const int te = (int)min<long long>(gr.ntiles, tb + (u1 - u));
     const int slot = (tb == 0 && te == gr.ntiles) ? -1 : (first ? 2 * w : 2 * w + 1);
-    attend_segment<D, PS, NW, MULTI>(p, gr, tbl, lds, pair, tb, te, slot);
+    attend_segment<D, NPS, NW, MULTI>(p, gr, tbl, lds, pair, tb, te, slot);
     u += te - tb;
     first = false;
     __syncthreads();  // the next segment's first rebuild reuses buffer 0
   }
 }
 
-template <int D, bool PS, int NW>
+template <int D, int NPS, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p, Grid gr) {
-  attn_bf16_body<D, PS, NW, false>(p, gr, nullptr);
+  attn_bf16_body<D, NPS, NW, false>(p, gr, nullptr);
 }
 
-template <int D, bool PS, int NW>
+template <int D, int NPS, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_multi_kernel(AttnParams p, Grid gr, PartTable tbl) {
-  attn_bf16_body<D, PS, NW, true>(p, gr, &tbl);
+  attn_bf16_body<D, NPS, NW, true>(p, gr, &tbl);
 }
 
 // Workgroup w whose units [w U / G, (w + 1) U / G) hold unit x (U >= G).
@@ -670,7 +682,7 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) 
   if (d0 == 0 && p.lse) p.lse[(int64_t)h * p.n_q + qi] = tot > 0.f ? M + __logf(tot) : -INFINITY;
 }
 
-template <int D, bool PS>
+template <int D, int NPS>
 hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream, const PartTable* parts) {
   constexpr int BM = 32 * kWaves;               // queries per workgroup
   const int max_wg = kAttnBf16MaxWorkgroups * 8 / kWaves;  // one CU's worth per 8 waves
@@ -711,10 +723,10 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream, const Pa
     if (er != hipSuccess) return er;
   }
   if (parts)
-    hipLaunchKernelGGL((attn_bf16_multi_kernel<D, PS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g,
+    hipLaunchKernelGGL((attn_bf16_multi_kernel<D, NPS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g,
                        tbl);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, PS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NPS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
@@ -726,9 +738,14 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream, const Pa
 
 hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream,
                                  const PartTable* parts) {
-  if (head_dim == 128)
-    return p.r > 0 ? launch_t<128, true>(p, heads, stream, parts) : launch_t<128, false>(p, heads, stream, parts);
-  return p.r > 0 ? launch_t<64, true>(p, heads, stream, parts) : launch_t<64, false>(p, heads, stream, parts);
+  // PSAC k-steps: none (r = 0), one (r <= 16) or two (r <= 32)
+  const int nps = p.r == 0 ? 0 : (p.r <= 16 ? 1 : 2);
+  if (head_dim == 128) {
+    if (nps == 0) return launch_t<128, 0>(p, heads, stream, parts);
+    return nps == 1 ? launch_t<128, 1>(p, heads, stream, parts) : launch_t<128, 2>(p, heads, stream, parts);
+  }
+  if (nps == 0) return launch_t<64, 0>(p, heads, stream, parts);
+  return nps == 1 ? launch_t<64, 1>(p, heads, stream, parts) : launch_t<64, 2>(p, heads, stream, parts);
 }
 
 }  // namespace qwm

@@ -31,7 +31,9 @@ int hip_fail(hipError_t e) {
 }
 
 int esize(const qwm_config* c) { return c->io_dtype == QWM_F32 ? 4 : 2; }
-int rpitch(int r) { return r == 0 ? 0 : (r <= 8 ? 8 : 16); }
+int rpitch(int r) { return r == 0 ? 0 : (r <= 8 ? 8 : (r <= 16 ? 16 : 32)); }
+// rows of the fp16 U^T block of the bf16 attention (one or two 16-row MFMA k-steps)
+int ut_rows(int r) { return r > 16 ? 32 : 16; }
 
 int check_config(const qwm_config* c) {
   if (!c) return QWM_ERR_INVALID_ARG;
@@ -47,7 +49,7 @@ int check_config(const qwm_config* c) {
   const int t = c->group_tokens;
   if (t != 1 && t != 2 && t != 4 && t != 8 && t != 16 && t != 32) return QWM_ERR_UNSUPPORTED;
   if (c->num_centroids_k > 512 || c->num_centroids_v > 512) return QWM_ERR_UNSUPPORTED;
-  if (c->top_candidates > 8 || c->rank > 16) return QWM_ERR_UNSUPPORTED;
+  if (c->top_candidates > 8 || c->rank > 32) return QWM_ERR_UNSUPPORTED;
   const int64_t cap = (int64_t)c->frame_tokens * c->max_frames;
   if (cap > (int64_t)1 << 30) return QWM_ERR_UNSUPPORTED;
   // codebook + start values must fit in LDS (160 KiB per workgroup)
@@ -82,7 +84,7 @@ void fill_layout(const qwm_config* c, qwm_layout_info* L) {
   put(L->head_max, H * 4 * 4);
   put(L->mu_k16, H * ck * D * 2);
   put(L->mu_v16, H * cv * D * 2);
-  put(L->ut16, H * 16 * D * 2);
+  put(L->ut16, H * ut_rows((int)r) * D * 2);
   put(L->moment, (c->flags & QWM_FULL_QUADRATIC) ? H * D * D * 8 : 0);
   L->calib_bytes = o;
   o = 0;
@@ -443,10 +445,11 @@ QWM_API int qwm_calib_import(const qwm_config* cfg, void* calib, const float* mu
     for (int j = 0; j < d; ++j) mk16[row * d + j] = f16(stored(mu_k, row * d + paired(j)));
   for (size_t row = 0; row < (size_t)H * cv; ++row)
     for (int j = 0; j < d; ++j) mv16[row * d + j] = f16(stored(mu_v, row * d + paired(j)));
+  const int utr = ut_rows(r);
   for (int h = 0; h < H; ++h)
-    for (int c = 0; c < 16; ++c)
+    for (int c = 0; c < utr; ++c)
       for (int j = 0; j < d; ++j)
-        ut16[((size_t)h * 16 + c) * d + j] = c < r ? f16(u[((size_t)h * d + paired(j)) * r + c]) : 0;
+        ut16[((size_t)h * utr + c) * d + j] = c < r ? f16(u[((size_t)h * d + paired(j)) * r + c]) : 0;
   // Blocking copy after draining the caller's stream: the block is complete
   // in device memory when this call returns.
   hipStream_t s = static_cast<hipStream_t>(stream);
