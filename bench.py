@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="matrix_game")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measures", action="store_true",
+                    help="skip the untimed quality measures (top-1 shift, logit MSE and the ablation appends), "
+                         "so that a profiler's per-kernel averages cover the timed launches only")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0: auto)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling for profiles)")
@@ -315,7 +318,8 @@ def main():
     loc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in el]))
     loc_tf = attn_flops(w, w.n_q, w.n_tokens + F) / (loc_ms * 1e-3) / 1e12
 
-    top1, logit_mse, stage2_ms = top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, args.seed, qwm, torch)
+    top1, logit_mse, stage2_ms = (None, None, None) if args.no_measures else \
+        top1_shift_per_mode(w, cfg, k, v, q, qh, kh, vh, args.seed, qwm, torch)
 
     stored, resident, original = qwm.footprint(cfg, w.n_tokens)
     res = {
@@ -370,7 +374,9 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = n * 4
     if not args.no_cpu_baseline:
-        heads = args.cpu_heads or max(1, min(w.heads, {"tiny": 1, "matrix_game": 2}.get(w.name, 1)))
+        # the whole Matrix-Game-2-like step (about 6 s of host work); one or
+        # two heads of the larger workloads, scaled to the full step
+        heads = args.cpu_heads or max(1, min(w.heads, {"tiny": 1, "matrix_game": w.heads}.get(w.name, 2)))
         res["cpu_baseline"] = cpu_baseline(w, data, cfg, heads, args.seed)
     print(json.dumps(res), flush=True)
 
