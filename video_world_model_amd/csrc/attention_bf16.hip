@@ -437,13 +437,21 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         // ---- S^T = K~ Q'^T: lane = query, keys 32mb + 8(i/4) + 4hf + i%4 ----
         f32x16 s[2];
         const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // K~ fragments read four ahead of their MFMA (a rolling window)
+        constexpr int NF = 2 * NKS;
+        auto frag = [&](int f) {
+          const int mb = f / NKS, ks = f % NKS;
+          return *reinterpret_cast<const h8_t*>(kt + (32 * mb + l32) * KROW + 16 * ks + 8 * hf);
+        };
+        h8_t win[4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int f = 0; f < 4; ++f) win[f] = frag(f);
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            const h8_t a = *reinterpret_cast<const h8_t*>(kt + (32 * mb + l32) * KROW + 16 * ks + 8 * hf);
-            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? zero16 : s[mb], 0, 0, 0);
-          }
+        for (int f = 0; f < NF; ++f) {
+          const int mb = f / NKS, ks = f % NKS;
+          const h8_t a = win[f & 3];
+          if (f + 4 < NF) win[f & 3] = frag(f + 4);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? zero16 : s[mb], 0, 0, 0);
         }
         // keep four K~ fragments in flight ahead of the MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -493,17 +501,23 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
         // rebuild of the next tile into the other buffer: independent VALU work
         // for the scheduler to place among the P V MFMAs
         rebuild((j + 1) & 1, ra);
-        // ---- O^T += V~^T P^T ----
+        // ---- O^T += V~^T P^T, V~ fragments read two MFMAs ahead ----
+        constexpr int NV = 4 * NDB;
+        auto vfrag = [&](int f) {
+          const int c = f / NDB, b = f % NDB;
+          const _Float16* va = vt + (16 * c + trow) * VROW + 32 * b + tcol;
+          const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va));
+          const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va + 8 * VROW));
+          return __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        h8_t vw[2] = {vfrag(0), vfrag(1)};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int b = 0; b < NDB; ++b) {
-            const _Float16* va = vt + (16 * c + trow) * VROW + 32 * b + tcol;
-            const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va));
-            const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va + 8 * VROW));
-            const h8_t a = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
-          }
+        for (int f = 0; f < NV; ++f) {
+          const int c = f / NDB, b = f % NDB;
+          const h8_t a = vw[f & 1];
+          if (f + 2 < NV) vw[f & 1] = vfrag(f + 2);
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
+        }
       } else {
         rebuild((j + 1) & 1, ra);
       }
