@@ -491,3 +491,56 @@ def test_epochs_single_equals_local():
     o_c, l_c = qwm.attention(cache, q)
     o_d, l_d = qwm.attention_epochs([cache], q)
     assert torch.equal(o_c, o_d) and torch.equal(l_c, l_d)
+
+
+def test_epochs_edge_cases():
+    """Sixteen epochs (the most one call takes; one frame each, several empty),
+    and epochs that are all empty with and without local keys."""
+    import torch
+    import video_world_model_amd as qwm
+    from oracle import attention as oa
+    w = workloads.scaled(W["matrix_game"], heads=1, frames=4)
+    cfg = P.cfg_of(w, max_frames=1)
+    F = w.frame_tokens
+    say("case epochs_edges")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    caches, rebuilt = [], []
+    frames = [0, None, 1, None, None, 2, None, None, None, None, 3, None, None, None, None, None]
+    for f in frames:
+        if f is None:
+            caches.append(_epoch_cache(cfg, cal, data["k"][:, :0], data["v"][:, :0]))
+            continue
+        k_e, v_e = data["k"][:, f * F:(f + 1) * F], data["v"][:, f * F:(f + 1) * F]
+        cache = _epoch_cache(cfg, cal, k_e, v_e)
+        caches.append(cache)
+        gpu = P.gpu_fields(cache, F)
+        stats = P.Stats()
+        ko = P.check_keys_head(cfg, k_e[0], cal, 0, gpu, stats)
+        vo = P.check_values_head(cfg, v_e[0], cal, 0, gpu, stats)
+        _, _, kr, vr = P.oracle_attention(cfg, cal, 0, ko, vo, data["q"][0][:1])
+        rebuilt.append((kr, vr))
+    assert len(caches) == 16
+    q = P.to_dev(data["q"][:, :200], cfg)
+    o, lse = qwm.attention_epochs(caches, q)
+    oo, ll = oa.attention_over_epochs(data["q"][0][:200], rebuilt)
+    kall = np.concatenate([kr for kr, _ in rebuilt])
+    vall = np.concatenate([vr for _, vr in rebuilt])
+    tol = np.maximum(2e-2, 2.0 ** -11 * np.abs(vall).max(axis=0))[None, :]
+    wo = float(np.max((np.abs(o[0].float().cpu().numpy() - oo) - P.bf16_half_ulp(oo)) / tol))
+    ltol = 1e-3 / np.sqrt(cfg.head_dim) * np.linalg.norm(data["q"][0][:200].astype(np.float64), axis=1) * \
+        np.linalg.norm(kall, axis=1).max()
+    wl = float(np.max(np.abs(lse[0].cpu().numpy() - ll) / ltol))
+    say("  16 epochs: %.3g %.3g" % (wo, wl))
+    assert wo <= 1.0 and wl <= 1.0
+    # every epoch empty: no keys (zeros, lse = -inf), or the local keys alone
+    empties = [c for c in caches if c.n_k == 0][:3]
+    o0, l0 = qwm.attention_epochs(empties, q)
+    assert float(o0.float().abs().max()) == 0.0 and bool(torch.isinf(l0).all())
+    k_loc = workloads.kv_frames(w, 0, "k", 4, 5)[None, :77]
+    v_loc = workloads.kv_frames(w, 0, "v", 4, 5)[None, :77]
+    o1, l1 = qwm.attention_epochs(empties, q, P.to_dev(k_loc, cfg), P.to_dev(v_loc, cfg))
+    wo, wl = check_local(cfg, cal, None, data["q"][:, :200], k_loc, v_loc, o1.float().cpu().numpy(),
+                         l1.cpu().numpy(), [0])
+    say("  empty epochs + local: %.3g %.3g" % (wo, wl))
+    assert wo <= 1.0 and wl <= 1.0
