@@ -276,6 +276,70 @@ def test_full_size_480p_sampled():
     say("  append parity ok: %s" % dict(stats))
 
 
+def test_full_size_matrix_game_all_heads():
+    """The Matrix-Game-2-like workload the default bench line times, at full
+    size (12 heads, 6 frames of 880 tokens, 880 queries) and in its launch
+    configuration: one fused K+V append of all frames, then attention with
+    the stream-K workspace, captured in a HIP graph and replayed.  Every head,
+    every append decision (tie following) and every query's output and lse
+    are checked against the oracle; so is the generation step with the next
+    frame as the local chunk."""
+    import torch
+    import video_world_model_amd as qwm
+    w = W["matrix_game"]
+    cfg = P.cfg_of(w)
+    say("case full_size_matrix_game: generating and calibrating (oracle)")
+    data = workloads.generate(w, threads=16)
+    cal = P.oracle_calibration(w, data, cfg, threads=16)
+    calib = qwm.alloc_calib(cfg)
+    qwm.calib_import(cfg, calib, cal["mu_k"], cal["mu_v"], cal["sens"], cal["u"])
+    cache = qwm.Cache(cfg, calib)
+    kd, vd, qd = P.to_dev(data["k"], cfg), P.to_dev(data["v"], cfg), P.to_dev(data["q"], cfg)
+    out = torch.empty_like(qd)
+    lse = torch.empty(cfg.heads, w.n_q, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qwm.workspace_bytes(cfg, w.n_tokens, w.n_q), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):  # warm-up outside the capture
+        cache.reset()
+        qwm.append_kv(cache, kd, vd)
+        qwm.attention(cache, qd, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cache.reset()
+        qwm.append_kv(cache, kd, vd)
+        qwm.attention(cache, qd, out=out, lse=lse, workspace=ws)
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    n = w.n_tokens
+    assert cache.n_k == n
+    gpu = P.gpu_fields(cache, n)
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    stats = P.Stats()
+    outs = []
+    worst_o = worst_l = 0.0
+    for h in range(cfg.heads):
+        ko = P.check_keys_head(cfg, data["k"][h], cal, h, gpu, stats)
+        vo = P.check_values_head(cfg, data["v"][h], cal, h, gpu, stats)
+        outs.append((ko, vo))
+        wo, wl = P.check_attention(cfg, cal, h, ko, vo, data["q"][h], o[h], l[h])
+        worst_o, worst_l = max(worst_o, wo), max(worst_l, wl)
+    say("  append parity ok: %s; attention max(|dO| - half ulp)/tol=%.3g max|dlse|/bound=%.3g"
+        % (dict(stats), worst_o, worst_l))
+    assert worst_o <= 1.0 and worst_l <= 1.0
+    k_loc = np.stack([workloads.kv_frames(w, h, "k", w.frames, w.frames + 1) for h in range(cfg.heads)])
+    v_loc = np.stack([workloads.kv_frames(w, h, "v", w.frames, w.frames + 1) for h in range(cfg.heads)])
+    o2, l2 = qwm.attention_local(cache, qd, P.to_dev(k_loc, cfg), P.to_dev(v_loc, cfg))
+    wo, wl = check_local(cfg, cal, outs, data["q"], k_loc, v_loc, o2.float().cpu().numpy(), l2.cpu().numpy(),
+                         range(cfg.heads))
+    say("  generation step with the local chunk: %.3g %.3g" % (wo, wl))
+    assert wo <= 1.0 and wl <= 1.0
+
+
 def check_local(cfg, cal, outs, q, k_loc, v_loc, o, lse, heads):
     """Attention over cache + local chunk against the oracle: worst output and
     lse errors over their bounds (the bounds of check_attention, taken over
