@@ -27,9 +27,11 @@
 //     otherwise the uncertain entries are rescored in fp64, four (token,
 //     centre) pairs at a time by the whole wave, or (rare) the wave searches
 //     all centres for the token.
-//  4. QSAC stage 2 scores the candidates' residual ranges in fp64; the INT2
-//     tile min/max is a DPP butterfly over the T lanes of a tile; PSAC
-//     accumulates c = U^T e in fp64 with U read wave-uniformly.
+//  4. QSAC stage 2 scores the candidates' residual ranges in fp64 (or, for
+//     the ablation scores, their one-token INT2 errors in the diagonal or the
+//     full quadratic form); the INT2 tile min/max is a DPP butterfly over the
+//     T lanes of a tile; PSAC accumulates c = U^T e in fp64 with U read
+//     wave-uniformly from LDS, in passes of at most 16 columns.
 #pragma once
 #include "qwm_internal.h"
 
