@@ -179,7 +179,7 @@ def cpu_baseline(w, data, cfg_host, heads, seed):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+        print("bench.py measures one GPU: the library runs on a single MI355X and has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
