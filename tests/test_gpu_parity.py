@@ -608,3 +608,56 @@ def test_epochs_edge_cases():
                          l1.cpu().numpy(), [0])
     say("  empty epochs + local: %.3g %.3g" % (wo, wl))
     assert wo <= 1.0 and wl <= 1.0
+
+
+def test_degenerate_inputs_zero_residual_and_tied_centres():
+    """Keys and Values that sit exactly on their centres (zero residual: every
+    tile scale 0, every code 0, every PSAC scale 0) mixed with ordinary tokens,
+    and a codebook with a duplicated centre (exact score ties, taken to the
+    lower index).  Append parity with tie following; where the residual is
+    zero the rebuilt keys equal the inputs, so attention over those tokens is
+    plain softmax attention over the bf16 keys."""
+    import torch
+    import video_world_model_amd as qwm
+    from oracle import attention as oa
+    w = workloads.scaled(W["matrix_game"], heads=2, frames=2)
+    cfg = P.cfg_of(w)
+    say("case degenerate_inputs")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    for key in ("mu_k", "mu_v"):  # centre 1 repeats centre 0
+        cal[key] = cal[key].copy()
+        cal[key][:, 1] = cal[key][:, 0]
+    rng = np.random.default_rng(3)
+    k, v = data["k"].copy(), data["v"].copy()
+    n = k.shape[1]
+    on = rng.random(n) < 0.75  # tokens placed on a centre (the first frame: all of them)
+    on[:w.frame_tokens] = True
+    for h in range(cfg.heads):
+        ck = rng.integers(0, cfg.c_k, n)
+        cv = rng.integers(0, cfg.c_v, n)
+        k[h, on] = cal["mu_k"][h][ck[on]]
+        v[h, on] = cal["mu_v"][h][cv[on]]
+    cache, _ = P.build_cache(cfg, cal, k, v)
+    gpu = P.gpu_fields(cache, n)
+    stats = P.Stats()
+    q = P.to_dev(data["q"], cfg)
+    o, lse = qwm.attention(cache, q)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    F, T = w.frame_tokens, w.group_tokens
+    for h in range(cfg.heads):
+        ko = P.check_keys_head(cfg, k[h], cal, h, gpu, stats)
+        vo = P.check_values_head(cfg, v[h], cal, h, gpu, stats)
+        # the first frame lies on centres: zero scales and codes in all its tiles
+        tiles0 = -(-F // T)
+        assert np.all(gpu["s_k"][h][:tiles0] == 0) and np.all(gpu["s_v"][h][:tiles0] == 0)
+        assert np.all(gpu["codes_k"][h][:F] == 0) and np.all(gpu["coef_scale"][h][:F] == 0)
+        wo, wl = P.check_attention(cfg, cal, h, ko, vo, data["q"][h], o[h], lse[h])
+        assert wo <= 1.0 and wl <= 1.0
+        # rebuilt keys and values of the first frame equal the inputs
+        _, _, kr, vr = P.oracle_attention(cfg, cal, h, ko, vo, data["q"][h][:1])
+        assert np.array_equal(kr[:F], k[h][:F].astype(np.float64))
+        assert np.array_equal(vr[:F], v[h][:F].astype(np.float64))
+    # a duplicated centre is never chosen over its first copy
+    assert not np.any(gpu["idx_v"] == 1)
+    say("  degenerate inputs ok: %s" % dict(stats))
