@@ -614,7 +614,7 @@ def test_degenerate_inputs_zero_residual_and_tied_centres():
     """Keys and Values that sit exactly on their centres (zero residual: every
     tile scale 0, every code 0, every PSAC scale 0) mixed with ordinary tokens,
     and a codebook with a duplicated centre (exact score ties, taken to the
-    lower index).  Append parity with tie following; where the residual is
+    lower index by both appends).  Append parity with tie following; where the residual is
     zero the rebuilt keys equal the inputs, so attention over those tokens is
     plain softmax attention over the bf16 keys."""
     import torch
@@ -658,6 +658,7 @@ def test_degenerate_inputs_zero_residual_and_tied_centres():
         _, _, kr, vr = P.oracle_attention(cfg, cal, h, ko, vo, data["q"][h][:1])
         assert np.array_equal(kr[:F], k[h][:F].astype(np.float64))
         assert np.array_equal(vr[:F], v[h][:F].astype(np.float64))
-    # a duplicated centre is never chosen over its first copy
-    assert not np.any(gpu["idx_v"] == 1)
+    # a duplicated centre is never chosen over its first copy (exact ties go
+    # to the lower index)
+    assert not np.any(gpu["idx_v"] == 1) and not np.any(gpu["idx_k"] == 1)
     say("  degenerate inputs ok: %s" % dict(stats))

@@ -542,13 +542,16 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
 
   int cand[KC];
   // tie-break value for QSAC stage 2 (smaller is better), on the -F scale:
-  // -key, or (D - ||k||_s^2) / 2 for centres that were rescored exactly
+  // -key with its index bits cleared (so that equal scores tie and the lower
+  // index wins, not the larger index field), or (D - ||k||_s^2) / 2 for
+  // centres that were rescored exactly
+  auto key_tie = [&](float key) { return -__uint_as_float(__float_as_uint(key) & ~mask); };
   float tieD[KC];
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     // clamp: only non-finite inputs can produce an index outside [0, C)
     cand[i] = min((int)(__float_as_uint(mylst[i]) & mask), C - 1);
-    tieD[i] = -mylst[i];
+    tieD[i] = key_tie(mylst[i]);
   }
 
   // D_c = sum_j s_j (k_j - mu_cj)^2 in fp64 for one centre, the row given by
@@ -685,7 +688,7 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
           const int c = min((int)(__float_as_uint(mylst[i]) & mask), C - 1);
 #pragma unroll
           for (int q = 0; q < KC; ++q)
-            if (q == n_sure) { cand[q] = c; tieD[q] = -mylst[i]; }
+            if (q == n_sure) { cand[q] = c; tieD[q] = key_tie(mylst[i]); }
           ++n_sure;
         }
       }
