@@ -381,6 +381,45 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def cpu_baseline_final_step(w, data, seed):
+    """The oracle (untuned) on the 1-minute rollout's final step for one head,
+    scaled to all heads: the append of the last frame plus attention of the
+    query chunk over every cached token.  The oracle's own append of the
+    earlier frames is the untimed setup."""
+    import numpy as np
+    from oracle import attention as oa
+    from oracle import calibrate as oc
+    from oracle import codec
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    F, T, n = w.frame_tokens, w.group_tokens, w.n_tokens
+    cal = oc.calibrate(data["q_hist"][:1], data["k_hist"][:1], data["v_hist"][:1], w.c_k, w.c_v, w.rank, w.io,
+                       seed=seed, iters=2)
+    mk, mv, sk, uk = cal["mu_k"][0], cal["mu_v"][0], cal["sens"][0], cal["u"][0]
+
+    def rebuilt(k, v):
+        ko = codec.append_keys(k, mk, sk, uk, F, T, w.top_k, 0)
+        vo = codec.append_values(v, mv, F, T)
+        kr = oa.reconstruct_keys(ko["idx"], ko["codes"], ko["z"], ko["s"], ko["coef"], ko["coef_scale"], mk, uk, F, T)
+        return kr, oa.reconstruct_values(vo["idx"], vo["codes"], vo["z"], vo["s"], mv, F, T)
+    k0, v0 = data["k"][0], data["v"][0]
+    kr_prev, vr_prev = rebuilt(k0[:n - F], v0[:n - F])
+    t0 = time.perf_counter()
+    kr_last, vr_last = rebuilt(k0[n - F:], v0[n - F:])
+    oa.softmax_attention(data["q"][0], np.concatenate([kr_prev, kr_last]), np.concatenate([vr_prev, vr_last]))
+    dt = time.perf_counter() - t0
+    step_s = dt * w.heads
+    return {"value": round(n / step_s / 1e3, 4), "unit": "Ktokens/s (final step: cached tokens / step time)",
+            "final_step_ms": round(step_s * 1e3, 1), "cores": int(min(cores, max(blas, 1))), "kind": "oracle",
+            "sample": "1 of %d heads at the final step (append of the last frame + attention of %d queries over %d "
+                      "cached tokens), %.1f s on the host, scaled x%d; the oracle's append of the earlier frames is "
+                      "untimed setup; BLAS threads %d, affinity cores %d" % (w.heads, w.n_q, n, dt, w.heads, blas, cores)}
+
+
 def rollout_epochs(args, w, cfg, ks, vs, q, qh, out, lse, ws, qwm, torch):
     """The 1-minute rollout with calibration epochs: every `epoch_frames`
     frames the library calibrates again (Query statistics from the query
@@ -498,6 +537,11 @@ def rollout(args, w, cfg, cache, reset, ks, vs, q, out, lse, ws, data, qwm, torc
     }
     if args.epoch_frames:
         res["calibration_epochs"] = rollout_epochs(args, w, cfg, ks, vs, q, qh, out, lse, ws, qwm, torch)
+    if not args.no_cpu_baseline:
+        print("[bench] oracle baseline of the final step (one head)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_final_step(w, data, args.seed)
+        # the GPU's final step in the same unit: last frame's append + attention
+        res["final_step_ktokens_s"] = round(w.n_tokens / ((float(app[-1]) + float(att[-1])) * 1e-3) / 1e3, 3)
     print(json.dumps(res), flush=True)
 
 
