@@ -233,6 +233,21 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
     return f;
   };
 
+  // U^T fragments of one calibration, the A operand of the MFMA that forms
+  // U^T q: rows 0..16 NPS - 1 are the directions (U^T has 16 NPS rows per
+  // head).  Lanes past them read the last row again; an A row only feeds its
+  // own output row, and those rows are not used.  All fragments are loaded
+  // before the first MFMA, so they cost one memory latency.
+  auto load_ut = [&](const uint16_t* ut16, h8_t(&a)[NG]) {
+    if constexpr (PS) {
+      const uint16_t* ut = ut16 + ((int64_t)h * 16 * NPS + min(l32, 16 * NPS - 1)) * D + 8 * hf;
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) a[ks] = *reinterpret_cast<const h8_t*>(ut + 16 * ks);
+    }
+  };
+  h8_t uta[NG];
+  if constexpr (!MULTI) load_ut(p.ut16, uta);  // in flight with the Query loads
+
   // ---- Q fragment [q | U^T q] in fp16, paired channel order ----
   h8_t qf[NKS];
   {
@@ -249,30 +264,22 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
                     bf_to_h(a.y & 0xffffu), bf_to_h(b.y & 0xffffu), bf_to_h(a.y >> 16), bf_to_h(b.y >> 16)};
     }
   }
-  // U^T q of one calibration into the PSAC k-steps of the Q fragment: rows
-  // 0..16 NPS - 1 of the 32-row MFMA are the directions (U^T has 16 NPS rows
-  // per head), accumulator values 8s..8s+7 fill PSAC k-step s
-  auto form_uq = [&](const uint16_t* ut16) {
+  // U^T q into the PSAC k-steps of the Q fragment: accumulator values
+  // 8s..8s+7 (output rows of directions 16s..16s+15) fill PSAC k-step s
+  auto form_uq = [&](const h8_t(&a)[NG]) {
     if constexpr (PS) {
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      const uint16_t* ut = ut16 + (int64_t)h * 16 * NPS * D;
 #pragma unroll
-      for (int ks = 0; ks < NG; ++ks) {
-        h8_t a;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = (_Float16)0.f;
-        if (l32 < 16 * NPS) a = *reinterpret_cast<const h8_t*>(ut + l32 * D + 16 * ks + 8 * hf);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], acc, 0, 0, 0);
-      }
+      for (int ks = 0; ks < NG; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[ks], acc, 0, 0, 0);
 #pragma unroll
       for (int s2 = 0; s2 < NPS; ++s2)
 #pragma unroll
         for (int i = 0; i < 8; ++i) qf[NG + s2][i] = (_Float16)acc[8 * s2 + i];
     }
   };
-  if constexpr (!MULTI) form_uq(p.ut16);
+  if constexpr (!MULTI) form_uq(uta);
 
   // ---- this thread's rebuild items ----
   bool it_v[IPT];
@@ -540,7 +547,8 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
       const int a = max(tb, cp.tile0), b = min(te, pend);
       if (a >= b) continue;
       const Fields f = fields_of(cp);
-      form_uq(f.ut16);
+      load_ut(f.ut16, uta);
+      form_uq(uta);
       uq = true;
       tile_loop(f, (a - cp.tile0) * BN, b - a, min(cp.n_k, (b - cp.tile0) * BN), std::false_type{});
     }
@@ -563,36 +571,59 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  if (!qvalid) return;
+  if (qvalid && hf == 0) {
+    if (slot >= 0)
+      p.part_ml[(int64_t)slot * kSlotRows + wave * 32 + l32] = lse;
+    else if (p.lse)
+      p.lse[(int64_t)h * p.n_q + qi] = lse;
+  }
+  // The wave's 32 output rows go through its own region of LDS (no wave
+  // reads the tile buffers after the loop's last barrier): written from the
+  // accumulators, then read back as 16-byte row pieces, so that each global
+  // store writes whole rows.  Final output in bf16; partials are O
+  // normalised by its own sum in fp16 (2^-11 relative, far below the bf16
+  // output's rounding), with the lse in fp32.
+  constexpr int EP = D + 8;  // fp16 pitch of a row in LDS
+  static_assert(NW * 32 * EP <= 2 * (BN * KROW + BN * VROW), "epilogue rows fit in the tile buffers");
+  uint16_t* ew = reinterpret_cast<uint16_t*>(lds) + wave * 32 * EP;
   // o[b][4 i4 + t] is stored position sp + t, sp = 32b + 8 i4 + 4hf: channels
   // ch, ch + 8, ch + 1, ch + 9 with ch = (sp & ~15) + (sp & 15) / 2
-  if (slot < 0) {
-    if (p.lse && hf == 0) p.lse[(int64_t)h * p.n_q + qi] = lse;
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + (int64_t)h * p.o_head_stride + (int64_t)qi * p.o_token_stride;
+  auto put_rows = [&](auto cvt) {
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int sp = 32 * b + 8 * i4 + 4 * hf;
         const int ch = (sp & ~15) + ((sp & 15) >> 1);
-        *reinterpret_cast<uint32_t*>(orow + ch) = pack_bf16(o[b][4 * i4] * inv, o[b][4 * i4 + 2] * inv);
-        *reinterpret_cast<uint32_t*>(orow + ch + 8) = pack_bf16(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
+        uint16_t* e = ew + l32 * EP + ch;
+        *reinterpret_cast<uint32_t*>(e) = cvt(o[b][4 * i4] * inv, o[b][4 * i4 + 2] * inv);
+        *reinterpret_cast<uint32_t*>(e + 8) = cvt(o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 3] * inv);
       }
-  } else {
-    // partials: O normalised by its own sum, in fp16 (2^-11 relative, far
-    // below the bf16 output's rounding), and the lse in fp32
-    const int64_t pb = (int64_t)slot * kSlotRows + wave * 32 + l32;
-    if (hf == 0) p.part_ml[pb] = lse;
-    uint16_t* prow = reinterpret_cast<uint16_t*>(p.part_o) + pb * D;
+  };
+  if (slot < 0)
+    put_rows([](float a, float b) { return pack_bf16(a, b); });
+  else
+    put_rows([](float a, float b) { return as_u32(h2_t{(_Float16)a, (_Float16)b}); });
+  // the rows are read back by other lanes of the same wave: LDS serves one
+  // wave's accesses in order, so only the compiler needs holding back
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // the lane index taken afresh: reusing the one from before the loop
+  // keeps it live through the loop, one more VGPR at the limit
+  const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  constexpr int PPR = D / 8;     // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;  // rows per store instruction
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int sp = 32 * b + 8 * i4 + 4 * hf;
-        const int ch = (sp & ~15) + ((sp & 15) >> 1);
-        *reinterpret_cast<uint32_t*>(prow + ch) = as_u32(h2_t{(_Float16)(o[b][4 * i4] * inv), (_Float16)(o[b][4 * i4 + 2] * inv)});
-        *reinterpret_cast<uint32_t*>(prow + ch + 8) = as_u32(h2_t{(_Float16)(o[b][4 * i4 + 1] * inv), (_Float16)(o[b][4 * i4 + 3] * inv)});
-      }
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int rr = i * RPI + ln / PPR, pc = ln % PPR;
+    const uint4 val = *reinterpret_cast<const uint4*>(ew + rr * EP + 8 * pc);
+    const int qr = q0 + rr;
+    if (qr < p.n_q) {
+      uint16_t* dst = slot < 0 ? static_cast<uint16_t*>(p.out) + (int64_t)h * p.o_head_stride + (int64_t)qr * p.o_token_stride
+                               : reinterpret_cast<uint16_t*>(p.part_o) + ((int64_t)slot * kSlotRows + wave * 32 + rr) * D;
+      *reinterpret_cast<uint4*>(dst + 8 * pc) = val;
+    }
   }
 }
 
@@ -643,39 +674,41 @@ __device__ __forceinline__ int wg_of(long long x, const Grid& gr) {
 }
 
 // Merges the partial results of a pair cut by workgroup boundaries: block
-// (pair, rows 8 blockIdx.y .. + 7 of its query block), 32 threads per row.
-// The contributors are workgroups wa..wb: wa holds the pair in its last
-// segment (its first, when its range starts at the pair), the others in
-// their first.  Online over the contributors, four at a time so that their
-// loads are in flight together:
+// (pair, rows kCombineRows<D> blockIdx.y .. of its query block), one thread
+// per 8 channels of a row (16-byte loads and stores).  The contributors are
+// workgroups wa..wb: wa holds the pair in its last segment (its first, when
+// its range starts at the pair), the others in their first.  Online over the
+// contributors, four at a time so that their loads are in flight together:
 //   o = sum_c exp(lse_c - M) o_c / sum_c exp(lse_c - M), lse = M + log sum.
 template <int D>
+constexpr int kCombineRows = 256 / (D / 8);  // rows per combine block
+
+template <int D>
 __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) {
-  constexpr int CPT = D / 32;  // channels per thread
+  constexpr int CPT = 8;        // channels per thread
+  constexpr int TPR = D / CPT;  // threads per row
   const int pair = blockIdx.x;
   const long long x0 = (long long)pair * gr.ntiles;
   const int wa = wg_of(x0, gr), wb = wg_of(x0 + gr.ntiles - 1, gr);
   if (wa == wb) return;  // one workgroup took the whole pair and wrote it
   const int qb = pair % gr.n_qb, h = pair / gr.n_qb;
-  const int r = blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int r = blockIdx.y * kCombineRows<D> + (int)threadIdx.x / TPR;
   const int rows = min(gr.qpb, p.n_q - qb * gr.qpb);
   if (r >= rows) return;
-  const int d0 = (threadIdx.x & 31) * CPT;
+  const int d0 = ((int)threadIdx.x % TPR) * CPT;
   const int slot_a = ((long long)wa * gr.units / gr.G >= x0) ? 2 * wa : 2 * wa + 1;
   float M = -INFINITY, tot = 0.f, acc[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) acc[j] = 0.f;
   for (int c0 = wa; c0 <= wb; c0 += 4) {
     float l[4];
-    _Float16 o[4][CPT];
+    h8_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int w = min(c0 + i, wb);
       const int64_t pb = (int64_t)(w == wa ? slot_a : 2 * w) * kSlotRows + r;
       l[i] = c0 + i <= wb ? p.part_ml[pb] : -INFINITY;
-      const _Float16* src = reinterpret_cast<const _Float16*>(p.part_o) + pb * D + d0;
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) o[i][j] = src[j];
+      o[i] = *reinterpret_cast<const h8_t*>(reinterpret_cast<const _Float16*>(p.part_o) + pb * D + d0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -690,9 +723,9 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) 
   }
   const int qi = qb * gr.qpb + r;
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  __bf16* dst = static_cast<__bf16*>(p.out) + (int64_t)h * p.o_head_stride + (int64_t)qi * p.o_token_stride + d0;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) dst[j] = (__bf16)(acc[j] * inv);
+  uint16_t* dst = static_cast<uint16_t*>(p.out) + (int64_t)h * p.o_head_stride + (int64_t)qi * p.o_token_stride + d0;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
+                                              pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv));
   if (d0 == 0 && p.lse) p.lse[(int64_t)h * p.n_q + qi] = tot > 0.f ? M + __logf(tot) : -INFINITY;
 }
 
@@ -744,7 +777,8 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream, const Pa
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
   if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
-  hipLaunchKernelGGL((combine_sk_kernel<D>), dim3((unsigned)pairs, (g.qpb + 7) / 8), dim3(256), 0, stream, p, g);
+  hipLaunchKernelGGL((combine_sk_kernel<D>), dim3((unsigned)pairs, (g.qpb + kCombineRows<D> - 1) / kCombineRows<D>),
+                     dim3(256), 0, stream, p, g);
   return hipGetLastError();
 }
 
