@@ -97,6 +97,11 @@ typedef struct qwm_config {
                                QWM_FULL_QUADRATIC */
   int32_t reserved;         /* must be 0 */
 } qwm_config;
+/* Every call rejects with QWM_ERR_UNSUPPORTED a config whose append working
+ * set does not fit one workgroup's 160 KiB of LDS: the larger codebook
+ * (padded to a multiple of 64 centres, rows of d + 8 elements; twice that
+ * for fp32 activations) plus fp64 U of the rank.  At d = 128 with bf16
+ * activations, C = 512 runs up to r = 16 and r = 32 needs C <= 448. */
 
 typedef struct qwm_strides {
   int64_t head;   /* elements between heads */

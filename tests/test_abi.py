@@ -59,6 +59,20 @@ def test_config_rejections(field, value, status):
     assert e.value.status == status
 
 
+def test_lds_limit_of_the_append_working_set():
+    """C = 512 with r = 32 (d = 128, bf16) does not fit one workgroup's LDS;
+    r = 16 at C = 512 and r = 32 at C = 448 do."""
+    w = workloads.WORKLOADS["lingbot720p"]
+    for c_k, rank, ok in ((512, 16, True), (448, 32, True), (512, 32, False)):
+        c = cfg_of(w, c_k=c_k, c_v=c_k, rank=rank)
+        if ok:
+            qwm.layout(c)
+        else:
+            with pytest.raises(qwm.QwmError) as e:
+                qwm.layout(c)
+            assert e.value.status == qwm.ERR_UNSUPPORTED
+
+
 def test_layout_alignment_and_sizes():
     for name, w in workloads.WORKLOADS.items():
         L = qwm.layout(cfg_of(w))
