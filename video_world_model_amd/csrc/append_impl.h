@@ -122,6 +122,28 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
                            : static_cast<const void*>(static_cast<const uint16_t*>(p.mu) + (int64_t)h * C * D);
 
   // ---- stage the codebook, the accumulator start values, s and U in LDS ----
+  // Start values, s and U: loaded first, unconditionally from clamped
+  // indices (a conditional load would wait for itself inside its branch), so
+  // that their latency overlaps the codebook's.
+  constexpr int IPT = (512 + NTH - 1) / NTH;                   // start values per thread (C <= 512)
+  constexpr int UPT = (D * (R > 0 ? R : 1) + NTH - 1) / NTH;  // U entries per thread
+  float iv[IPT];
+  double uv[UPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const int c = u * NTH + (int)threadIdx.x;
+    iv[u] = p.norm_half[(int64_t)h * C + min(c, C - 1)];
+  }
+  const int jt = min((int)threadIdx.x, D - 1);
+  float sj = p.sens[(int64_t)h * D + jt];  // the block holds s also under QWM_UNIFORM_SENS
+  if constexpr (KEY && R > 0) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int e = u * NTH + (int)threadIdx.x;
+      uv[u] = p.u64[(int64_t)h * D * R + min(e, D * R - 1)];
+    }
+  }
+
   // bf16 codebooks: every global load of a thread is issued before its LDS
   // stores, so staging costs about one memory latency (16 row chunks per
   // thread cover every supported C in one round)
@@ -159,29 +181,12 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
     }
   }
   {
-    constexpr int IPT = (512 + NTH - 1) / NTH;                   // start values per thread (C <= 512)
-    constexpr int UPT = (D * (R > 0 ? R : 1) + NTH - 1) / NTH;  // U entries per thread
-    float iv[IPT];
-    double uv[UPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const int c = u * NTH + (int)threadIdx.x;
-      iv[u] = c < C ? -p.norm_half[(int64_t)h * C + c] : -3.0e38f;
+      if (c < Cpad) init[c] = c < C ? -iv[u] : -3.0e38f;
     }
-    const int jt = min((int)threadIdx.x, D - 1);
-    const float sj = p.uniform ? 1.f : p.sens[(int64_t)h * D + jt];
-    if constexpr (KEY && R > 0) {
-#pragma unroll
-      for (int u = 0; u < UPT; ++u) {
-        const int e = u * NTH + (int)threadIdx.x;
-        uv[u] = e < D * R ? p.u64[(int64_t)h * D * R + e] : 0.0;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int c = u * NTH + (int)threadIdx.x;
-      if (c < Cpad) init[c] = iv[u];
-    }
+    if (p.uniform) sj = 1.f;
     if ((int)threadIdx.x < D) s_lds[threadIdx.x] = sj;
     if constexpr (KEY && R > 0) {
 #pragma unroll
