@@ -1,4 +1,5 @@
 """Pins of the oracle's calibration step (CPU only)."""
+import json
 import os
 
 import numpy as np
@@ -68,6 +69,21 @@ def test_forgy_indices_distinct():
     idx = oc.forgy_indices(100, 40, 12345)
     assert len(set(idx.tolist())) == 40 and idx.min() >= 0 and idx.max() < 100
     assert np.array_equal(idx, oc.forgy_indices(100, 40, 12345))
+
+
+def test_forgy_indices_hand_worked():
+    """The initialiser against an index list worked out by hand from the
+    published SplitMix64 seed-0 outputs (swap partner i + next() mod (n - i);
+    a partner drawn mod n, or a shuffle of the full range, gives another list)."""
+    g = json.load(open(os.path.join(GOLDEN, "forgy_seed0.json")))
+    assert oc.forgy_indices(g["n"], g["c"], g["seed"]).tolist() == g["indices"]
+    # C = n: the full shuffle is a permutation whose first three slots are the same
+    full = oc.forgy_indices(g["n"], g["n"], g["seed"]).tolist()
+    assert sorted(full) == list(range(g["n"])) and full[:3] == g["indices"]
+    # k-means starts from these rows (seed + 2h for Keys of head h)
+    x = np.arange(10, dtype=np.float64)[:, None] * np.ones((1, 4))
+    mu, _ = oc.kmeans(x, 3, 0, seed=0)
+    assert mu[:, 0].tolist() == [5.0, 1.0, 9.0]
 
 
 def test_kmeans_objective_non_increasing_and_bruteforce_assign():

@@ -336,3 +336,58 @@ def test_epoch_keys_keep_their_own_calibration():
         worst_other = max(worst_other, float(oth.max()))
     assert worst_own <= 1e-4
     assert worst_other > 1e-2
+
+
+def test_qsac_hand_worked_candidates_and_choice():
+    """Stage 1 and stage 2 on a hand-worked example whose distances and
+    range scores are exact binary fractions: the candidate lists (K_c
+    smallest D, the lower index first at a tie) and the final choice for
+    K_c = 1..5, with per-channel and with uniform sensitivities."""
+    g = json.load(open(os.path.join(GOLDEN, "qsac_worked.json")))
+    d = g["d"]
+    mu = np.zeros((len(g["centres"]), d), np.float32)
+    for c, row in g["centres"].items():
+        for j, val in row.items():
+            mu[int(c), int(j)] = val
+    k = np.zeros((1, d), np.float32)
+    s = np.array(g["sens"], np.float32)
+    _, info = codec.select_keys(k, mu, s, 5, 0)
+    assert info["D"][0].tolist() == g["D"]
+    assert (info["P"][0] * 108).tolist() == [g["P_times_108"][c] for c in info["cand"][0]]
+    for case in g["cases"]:
+        flags = codec.UNIFORM_SENS if case["uniform"] else 0
+        idx, info = codec.select_keys(k, mu, s, case["top_k"], flags)
+        assert info["cand"][0].tolist() == case["cand"], case
+        assert int(idx[0]) == case["choice"], case
+    # argmin modes take the nearest centre whatever K_c is
+    for flags in (codec.NO_RANGE_TERM,):
+        idx, _ = codec.select_keys(k, mu, s, 4, flags)
+        assert int(idx[0]) == 0
+    idx, _ = codec.select_keys(k, mu, s, 0, 0)
+    assert int(idx[0]) == 0
+
+
+@pytest.mark.parametrize("top_k", [2, 4, 8])
+def test_candidate_sets_equal_bruteforce_sort(tiny, top_k):
+    """K_c < C: the candidate set of every token is the first K_c entries of a
+    brute-force sort of (D, c) computed with scalar loops, and the choice is
+    the brute-force minimum of (P, D, c) over those candidates only."""
+    w, d, cal = tiny
+    k, mu, s = d["k"][0], cal["mu_k"][0], cal["sens"][0].astype(np.float64)
+    n_c = mu.shape[0]
+    assert top_k < n_c
+    sg = [sum(s[16 * g:16 * g + 16]) for g in range(4)]
+    idx, info = codec.select_keys(k, mu, s, top_k, 0)
+    for t in range(0, k.shape[0], 3):
+        dd = [sum(s[j] * (float(k[t, j]) - float(mu[c, j])) ** 2 for j in range(64)) for c in range(n_c)]
+        order = sorted(range(n_c), key=lambda c: (dd[c], c))
+        assert info["cand"][t].tolist() == order[:top_k]
+        best = None
+        for c in order[:top_k]:
+            rho = [float(np.float32(float(k[t, j]) - float(mu[c, j]))) for j in range(64)]
+            p = sum(sg[g] * (max(rho[16 * g:16 * g + 16]) - min(rho[16 * g:16 * g + 16])) ** 2
+                    for g in range(4)) / 108.0
+            key = (p, dd[c], c)
+            if best is None or key < best:
+                best = key
+        assert idx[t] == best[2]

@@ -158,6 +158,10 @@ def calibrate_host(cfg: Config, q_hist, k_hist, v_hist, seed: int, iters: int = 
     """Host calibration from numpy [H, n, d] arrays (io-precision values)."""
     q, k, v = _f32(q_hist), _f32(k_hist), _f32(v_hist)
     H, d = cfg.heads, cfg.head_dim
+    if q.ndim != 3 or q.shape[0] != H or q.shape[2] != d:
+        raise ValueError("q_hist: shape %s, expected [%d, n, %d]" % (q.shape, H, d))
+    if k.ndim != 3 or k.shape[0] != H or k.shape[2] != d or v.shape != k.shape:
+        raise ValueError("k_hist / v_hist: shapes %s / %s, expected [%d, n, %d] each" % (k.shape, v.shape, H, d))
     out = dict(mu_k=np.zeros((H, cfg.c_k, d), np.float32), mu_v=np.zeros((H, cfg.c_v, d), np.float32),
                sens=np.zeros((H, d), np.float32), u=np.zeros((H, d, max(cfg.rank, 1)), np.float32),
                energy=np.zeros(H, np.float64))
@@ -189,6 +193,53 @@ def strides(t) -> QwmStrides:
     return QwmStrides(t.stride(0), t.stride(1))
 
 
+def check_activation(cfg: Config, t, name: str, n_tokens=None):
+    """Raises ValueError unless t is a [heads, n, head_dim] tensor of the
+    config's I/O dtype on a GPU, with a contiguous head_dim axis (and, when
+    given, n == n_tokens).  The library dereferences the pointer on the
+    device, so a host tensor, too few heads or a narrower dtype would read
+    outside the allocation."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s: expected a torch tensor" % name)
+    if t.dtype != cfg.torch_dtype:
+        raise ValueError("%s: dtype %s, the config's activations are %s" % (name, t.dtype, cfg.torch_dtype))
+    if t.dim() != 3 or t.shape[0] != cfg.heads or t.shape[2] != cfg.head_dim:
+        raise ValueError("%s: shape %s, expected [%d, n, %d]" % (name, tuple(t.shape), cfg.heads, cfg.head_dim))
+    if n_tokens is not None and t.shape[1] != n_tokens:
+        raise ValueError("%s: %d tokens, expected %d" % (name, t.shape[1], n_tokens))
+    if t.stride(2) != 1:
+        raise ValueError("%s: the head_dim axis must be contiguous" % name)
+    if not t.is_cuda:
+        raise ValueError("%s: the tensor is not in GPU memory" % name)
+
+
+def check_device_buffer(t, name: str, dtype, shape=None, min_bytes=None):
+    """Raises ValueError unless t is a contiguous GPU tensor of dtype (and of
+    the given shape, or at least min_bytes long)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s: expected a torch tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError("%s: %d bytes, at least %d needed" % (name, t.numel() * t.element_size(), min_bytes))
+    if not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s: the tensor is not in GPU memory" % name)
+
+
+def _check_outputs(cfg, q, out, lse, workspace):
+    import torch
+    check_activation(cfg, out, "out", q.shape[1])
+    check_device_buffer(lse, "lse", torch.float32, shape=(cfg.heads, q.shape[1]))
+    if workspace is not None:
+        check_device_buffer(workspace, "workspace", torch.uint8)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
 
@@ -198,7 +249,19 @@ def alloc_calib(cfg: Config, device="cuda"):
     return torch.empty(layout(cfg)["calib_bytes"], dtype=torch.uint8, device=device)
 
 
+def _check_calib(cfg: Config, calib):
+    import torch
+    check_device_buffer(calib, "calib", torch.uint8, min_bytes=layout(cfg)["calib_bytes"])
+
+
 def calib_import(cfg: Config, calib, mu_k, mu_v, sens, u):
+    _check_calib(cfg, calib)
+    H, d, r = cfg.heads, cfg.head_dim, cfg.rank
+    for name, a, shape in (("mu_k", mu_k, (H, cfg.c_k, d)), ("mu_v", mu_v, (H, cfg.c_v, d)), ("sens", sens, (H, d))):
+        if np.shape(a) != shape:
+            raise ValueError("%s: shape %s, expected %s" % (name, np.shape(a), shape))
+    if r and np.shape(u) != (H, d, r):
+        raise ValueError("u: shape %s, expected %s" % (np.shape(u), (H, d, r)))
     c = cfg.c()
     arrs = [_f32(mu_k), _f32(mu_v), _f32(sens), _f32(u if cfg.rank else np.zeros(1))]
     check(lib().qwm_calib_import(ctypes.byref(c), _ptr(calib), *[a.ctypes.data_as(ctypes.c_void_p) for a in arrs],
@@ -207,6 +270,7 @@ def calib_import(cfg: Config, calib, mu_k, mu_v, sens, u):
 
 def calib_import_moment(cfg: Config, calib, m):
     """Full Query second moment [H][d][d] (float64) for FULL_QUADRATIC configs."""
+    _check_calib(cfg, calib)
     c = cfg.c()
     a = np.ascontiguousarray(m, dtype=np.float64)
     if a.shape != (cfg.heads, cfg.head_dim, cfg.head_dim):
@@ -216,6 +280,12 @@ def calib_import_moment(cfg: Config, calib, m):
 
 def calibrate(cfg: Config, calib, q_hist, k_hist, v_hist, seed: int, iters: int = 10):
     """Device calibration; returns the per-head energy fraction (numpy)."""
+    _check_calib(cfg, calib)
+    check_activation(cfg, q_hist, "q_hist")
+    check_activation(cfg, k_hist, "k_hist")
+    check_activation(cfg, v_hist, "v_hist", k_hist.shape[1])
+    if k_hist.stride() != v_hist.stride():
+        raise ValueError("k_hist and v_hist must have the same strides")
     c = cfg.c()
     energy = np.zeros(cfg.heads, np.float64)
     sq, skv = strides(q_hist), strides(k_hist)
@@ -229,6 +299,7 @@ class Cache:
     """A compressed cache: owns its device block and the host handle."""
 
     def __init__(self, cfg: Config, calib, device="cuda"):
+        _check_calib(cfg, calib)
         torch = _torch()
         self.cfg = cfg
         self.layout = layout(cfg)
@@ -275,6 +346,7 @@ class Cache:
 
 
 def append_k(cache: Cache, k):
+    check_activation(cache.cfg, k, "k")
     c = cache.cfg.c()
     s = strides(k)
     check(lib().qwm_quantize_append_k(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(k), k.shape[1],
@@ -282,6 +354,7 @@ def append_k(cache: Cache, k):
 
 
 def append_v(cache: Cache, v):
+    check_activation(cache.cfg, v, "v")
     c = cache.cfg.c()
     s = strides(v)
     check(lib().qwm_quantize_append_v(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(v), v.shape[1],
@@ -291,8 +364,11 @@ def append_v(cache: Cache, v):
 def append_kv(cache: Cache, k, v):
     """Keys and Values of the same tokens in one launch (same fields as
     append_k then append_v)."""
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape")
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError("k and v: shapes %s and %s differ (the same tokens are appended)"
+                         % (tuple(k.shape), tuple(v.shape)))
+    check_activation(cache.cfg, k, "k")
+    check_activation(cache.cfg, v, "v", k.shape[1])
     c = cache.cfg.c()
     sk, sv = strides(k), strides(v)
     check(lib().qwm_quantize_append_kv(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(k), _ptr(v), k.shape[1],
@@ -308,8 +384,9 @@ def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float 
     """Attention of q over the cache.  kernel_events: optional pair of
     torch.cuda.Event (already recorded once, so that they exist) that the
     library records around the main attention kernel alone."""
-    torch = _torch()
     cfg = cache.cfg
+    check_activation(cfg, q, "q")
+    torch = _torch()
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -317,6 +394,7 @@ def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float 
     if workspace is None:
         nb = workspace_bytes(cfg, cache.n_k, q.shape[1])
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    _check_outputs(cfg, q, out, lse, workspace)
     c = cfg.c()
     sq, so = strides(q), strides(out)
     nb = workspace.numel() if workspace is not None else 0
@@ -336,11 +414,12 @@ def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float 
 def attention_local(cache: Cache, q, k_loc, v_loc, out=None, lse=None, workspace=None, scale: float = 0.0):
     """Attention of the query chunk q over the compressed cache and the chunk's
     own uncompressed keys and values k_loc, v_loc [H][n_loc][d] (bf16)."""
-    torch = _torch()
     cfg = cache.cfg
+    check_activation(cfg, q, "q")
+    check_activation(cfg, k_loc, "k_loc")
     n_loc = k_loc.shape[1]
-    if v_loc.shape[1] != n_loc:
-        raise ValueError("k_loc and v_loc hold different token counts")
+    check_activation(cfg, v_loc, "v_loc", n_loc)
+    torch = _torch()
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -348,6 +427,7 @@ def attention_local(cache: Cache, q, k_loc, v_loc, out=None, lse=None, workspace
     if workspace is None:
         nb = workspace_bytes(cfg, cache.n_k + n_loc, q.shape[1])
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    _check_outputs(cfg, q, out, lse, workspace)
     c = cfg.c()
     sq, sk, sv, so = strides(q), strides(k_loc), strides(v_loc), strides(out)
     nb = workspace.numel() if workspace is not None else 0
@@ -362,11 +442,15 @@ def attention_epochs(caches, q, k_loc=None, v_loc=None, out=None, lse=None, work
     """Attention of the query chunk q over the compressed caches of successive
     calibration epochs (a list of Cache, oldest first, same Config) and,
     optionally, the chunk's own keys and values k_loc, v_loc (bf16)."""
-    torch = _torch()
     cfg = caches[0].cfg
+    if any(c.cfg != cfg for c in caches):
+        raise ValueError("every epoch's cache must have the same Config")
+    check_activation(cfg, q, "q")
     n_loc = 0 if k_loc is None else k_loc.shape[1]
-    if n_loc and v_loc.shape[1] != n_loc:
-        raise ValueError("k_loc and v_loc hold different token counts")
+    if n_loc:
+        check_activation(cfg, k_loc, "k_loc")
+        check_activation(cfg, v_loc, "v_loc", n_loc)
+    torch = _torch()
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -375,6 +459,7 @@ def attention_epochs(caches, q, k_loc=None, v_loc=None, out=None, lse=None, work
     if workspace is None:
         nb = workspace_bytes(cfg, total + n_loc, q.shape[1])
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    _check_outputs(cfg, q, out, lse, workspace)
     handles = (QwmCache * len(caches))(*[c.handle for c in caches])
     c = cfg.c()
     sq, so = strides(q), strides(out)
@@ -388,8 +473,9 @@ def attention_epochs(caches, q, k_loc=None, v_loc=None, out=None, lse=None, work
 
 
 def attention_logits(cache: Cache, q, scale: float = 0.0):
-    torch = _torch()
     cfg = cache.cfg
+    check_activation(cfg, q, "q")
+    torch = _torch()
     lg = torch.empty(cfg.heads, q.shape[1], cache.n_k, dtype=torch.float32, device=q.device)
     c = cfg.c()
     sq = strides(q)
@@ -399,8 +485,9 @@ def attention_logits(cache: Cache, q, scale: float = 0.0):
 
 
 def top1(cache: Cache, q):
-    torch = _torch()
     cfg = cache.cfg
+    check_activation(cfg, q, "q")
+    torch = _torch()
     out = torch.empty(cfg.heads, q.shape[1], dtype=torch.int32, device=q.device)
     c = cfg.c()
     sq = strides(q)
@@ -410,6 +497,8 @@ def top1(cache: Cache, q):
 
 
 def dense_top1(cfg: Config, q, k):
+    check_activation(cfg, q, "q")
+    check_activation(cfg, k, "k")
     torch = _torch()
     out = torch.empty(cfg.heads, q.shape[1], dtype=torch.int32, device=q.device)
     c = cfg.c()
