@@ -157,7 +157,9 @@ typedef struct qwm_layout_info {
   uint32_t idx_k_bytes, idx_v_bytes;
 } qwm_layout_info;
 
-/* Host handle of one compressed cache.  Fill with qwm_cache_init. */
+/* Host handle of one compressed cache.  Fill with qwm_cache_init.  The
+ * caller owns it: lowering n_k and n_v together to a smaller whole number of
+ * frames drops the newest frames (the next append overwrites them). */
 typedef struct qwm_cache {
   void* base;          /* device, layout.cache_bytes */
   const void* calib;   /* device, layout.calib_bytes */
@@ -283,6 +285,17 @@ int qwm_quantize_append_kv(const qwm_config* cfg, qwm_cache* cache, const void* 
                            const void* v_new, int64_t n_new, const qwm_strides* st_k,
                            const qwm_strides* st_v, void* stream);
 
+/* Test and measurement hook: appends enqueued after this call add, with
+ * device atomics, to counters (device uint32[4], nullable to stop; 4-byte
+ * aligned): [0] Key tokens whose candidate set the append settled by exact
+ * fp64 rescoring of the screen's uncertain band, [1] Key tokens that
+ * searched all centres because the tracked list could not hold every
+ * possible candidate, [2] and [3] the same for Values.  The pointer is a
+ * process-wide setting read when each append is enqueued (graph-captured
+ * appends keep the pointer they were captured with); set it from one thread
+ * with no append in flight on another.  The caller clears the counters. */
+int qwm_append_path_counters(void* counters);
+
 /* Workspace bytes qwm_attention may use for n_q queries over n_tokens cached
  * tokens: partial results of query blocks whose key range is divided among
  * workgroups (bf16 activations: a fixed 2 x 256 slots of 256 rows, fp16, about
@@ -367,8 +380,12 @@ int qwm_attention_epochs(const qwm_config* cfg, const qwm_cache* caches, int32_t
                          const qwm_strides* st_k, const qwm_strides* st_v, float scale, void* out,
                          const qwm_strides* st_out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
-/* The logits l [H][n_q][n_k] fp32 of the same kernel (debug variant), for
- * logit parity checks on small shapes. */
+/* The logits l = scale q.k~ [H][n_q][n_k] fp32 (scale 1/sqrt(d) when <= 0),
+ * exported by a debug variant of the attention kernel the activations' dtype
+ * selects: the same tile rebuild and the same contraction S = Q' K~^T (for
+ * bf16 activations: binary16 operands, fp32 accumulation), for logit parity
+ * checks on small shapes ([abstract]: the logits Q K^T are the quantity the
+ * method protects).  n_k = 0 or n_q = 0: nothing is written. */
 int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, const void* q,
                          int64_t n_q, const qwm_strides* st_q, float scale, float* logits,
                          void* stream);
@@ -378,7 +395,9 @@ int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, const vo
  * queries whose highest-scoring historical token changes).  qwm_top1 writes
  * argmax_t q.k~_t over the compressed cache; qwm_dense_top1 writes argmax_t
  * q.k_t over original keys k [H][n_k][d] (io dtype).  Both: int32 [H][n_q],
- * ties to the lowest t, fp32 dot products of the io values.
+ * ties to the lowest t.  qwm_top1 takes the scores S of the attention
+ * kernel's top-1 variant (the rebuild and contraction of qwm_attention_logits);
+ * qwm_dense_top1 takes fp32 dot products of the io values.
  */
 int qwm_top1(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
              const qwm_strides* st_q, int32_t* top1, void* stream);

@@ -32,7 +32,9 @@ Readings (the pages are silent)
 Pins (tests/test_oracle_calibrate.py): Eq. 7 identity on random e; LAPACK eigh
 against an independent subspace iteration; generator energy ~0.70; k-means
 objective non-increasing, zero with C = n distinct points, assignments equal a
-brute-force nearest search; SplitMix64 against its published seed-0 outputs.
+brute-force nearest search; SplitMix64 against its published seed-0 outputs;
+the Forgy indices against a list worked out by hand from those outputs
+(tests/golden/forgy_seed0.json).
 """
 import numpy as np
 

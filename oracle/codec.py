@@ -45,7 +45,11 @@ Pins (tests/test_oracle_codec.py): invariant (a) QVG_MODE = brute-force nearest
 centre; invariant (b) |rho - rho_hat| <= range/6 + rounding slack; invariant
 (c) rank 0 = QVG reconstruction, rank d removes the Key error up to INT8
 rounding; invariant (d) K_c = C equals a brute-force global argmin of P;
-INT2 idempotence; a hand-worked INT2/INT8 example under tests/golden.
+INT2 idempotence; a hand-worked INT2/INT8 example under tests/golden; a
+hand-worked QSAC example (tests/golden/qsac_worked.json: candidate lists and
+choices for K_c = 1..5, per-channel and uniform sensitivities); for K_c < C,
+candidate sets equal to a brute-force sort of (D, c) and the choice the
+brute-force minimum of (P, D, c) among them.
 """
 import math
 

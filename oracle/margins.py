@@ -19,6 +19,10 @@ Kinds
   sigma  : distance of fl32(a/127) to the nearest binary16 midpoint / sigma
   int8   : |c32/sigma - (n + 1/2)| sigma / a for the nearest half-integer
            (sigma and int8 are reported only: they are exact functions of c32)
+
+Pins (tests/test_oracle_margins.py): values placed exactly on and at known
+distances from binary32 and binary16 rounding midpoints, half-integer INT8
+ratios, exact and near ties of D and P with binary-exact gaps.
 """
 import numpy as np
 

@@ -20,7 +20,9 @@ Top-1 shift (digest, attention-analysis paragraph): the share of
 (head, query) pairs whose highest-scoring historical token under the
 reconstructed Keys differs from the one under the original Keys (float64
 logits, ties to the lowest token index).  Parity unpinned against the pages'
-53.88 % -> 10.19 % etc. (real models); pinned to 0 for zero-residual keys.
+53.88 % -> 10.19 % etc. (real models); pinned to 0 for zero-residual keys
+and to a hand-worked four-query case with a known shift of 1/4 that a
+last-maximum tie rule would get wrong (tests/test_oracle_margins.py).
 """
 import math
 

@@ -24,7 +24,8 @@ UNIFORM_SENS, NO_RANGE_TERM, QVG_MODE, EXACT_ERROR, FULL_QUADRATIC = 1, 2, 3, 4,
 EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint", "qwm_calibrate_host",
            "qwm_calib_import", "qwm_calib_import_moment", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
            "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention",
-           "qwm_attention_timed", "qwm_attention_local", "qwm_attention_epochs", "qwm_attention_logits", "qwm_top1", "qwm_dense_top1"]
+           "qwm_attention_timed", "qwm_attention_local", "qwm_attention_epochs", "qwm_attention_logits", "qwm_top1", "qwm_dense_top1",
+           "qwm_append_path_counters"]
 
 
 class QwmConfig(ctypes.Structure):
@@ -96,6 +97,7 @@ def lib():
             "qwm_attention_logits": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, P]),
             "qwm_top1": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P]),
             "qwm_dense_top1": (ctypes.c_int, [CFG, P, I64, ST, P, I64, ST, P, P]),
+            "qwm_append_path_counters": (ctypes.c_int, [P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -298,16 +300,32 @@ def calibrate(cfg: Config, calib, q_hist, k_hist, v_hist, seed: int, iters: int 
 class Cache:
     """A compressed cache: owns its device block and the host handle."""
 
-    def __init__(self, cfg: Config, calib, device="cuda"):
+    def __init__(self, cfg: Config, calib, device="cuda", base=None):
+        """base: optional caller-provided uint8 GPU tensor of at least the
+        layout's cache bytes (else one is allocated)."""
         _check_calib(cfg, calib)
         torch = _torch()
         self.cfg = cfg
         self.layout = layout(cfg)
         self.calib = calib
-        self.base = torch.empty(self.layout["cache_bytes"], dtype=torch.uint8, device=device)
+        if base is None:
+            base = torch.empty(self.layout["cache_bytes"], dtype=torch.uint8, device=device)
+        check_device_buffer(base, "base", torch.uint8, min_bytes=self.layout["cache_bytes"])
+        self.base = base
         self.handle = QwmCache()
         c = cfg.c()
         check(lib().qwm_cache_init(ctypes.byref(c), _ptr(calib), _ptr(self.base), ctypes.byref(self.handle)))
+
+    def truncate(self, n_tokens: int):
+        """Drop the newest frames: both counters back to n_tokens (a whole
+        number of frames, at most the current count); the next append
+        overwrites the dropped tokens.  Host-side only."""
+        F = self.cfg.frame_tokens
+        if n_tokens < 0 or n_tokens % F or n_tokens > min(self.handle.n_k, self.handle.n_v):
+            raise ValueError("truncate to %d tokens: not a whole number of frames at most the cached %d"
+                             % (n_tokens, min(self.handle.n_k, self.handle.n_v)))
+        self.handle.n_k = n_tokens
+        self.handle.n_v = n_tokens
 
     def reset(self):
         """Empty the cache (counters to zero; the next appends overwrite it)."""
@@ -506,3 +524,13 @@ def dense_top1(cfg: Config, q, k):
     check(lib().qwm_dense_top1(ctypes.byref(c), _ptr(q), q.shape[1], ctypes.byref(sq), _ptr(k), k.shape[1],
                                ctypes.byref(sk), _ptr(out), _stream()))
     return out
+
+
+def append_path_counters(counters):
+    """Appends enqueued from now on add their path counts to counters (a GPU
+    int32 tensor of 4: Key tokens settled by band rescoring, Key tokens that
+    searched all centres, then the same for Values); None stops counting."""
+    import torch
+    if counters is not None:
+        check_device_buffer(counters, "counters", torch.int32, shape=(4,))
+    check(lib().qwm_append_path_counters(_ptr(counters)))

@@ -609,6 +609,7 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
     if (!sure && !out && mylst[i] > -INFINITY) band_bits |= 1u << i;
   }
   if (__any(need_band)) {
+    if (p.counters && lane == 0) atomicAdd(p.counters + (KEY ? 0 : 2), (uint32_t)__popcll(__ballot(need_band)));
     reset_best();
     // Requests (lane t, tracked entry i) are served four at a time by the
     // whole wave: request q takes lanes 16q..16q+15, each summing CPL channels
@@ -717,6 +718,7 @@ __device__ __forceinline__ void append_body(const AppendParams& p, int bx) {
   // whole wave searches all centres for one such token at a time: its row is
   // broadcast to scalar registers and lane l scores centres l, l+64, ...
   uint64_t full = __ballot(!certain && !list_covers && valid);
+  if (p.counters && full && lane == 0) atomicAdd(p.counters + (KEY ? 1 : 3), (uint32_t)__popcll(full));
   while (full) {
     const int t = __builtin_ctzll(full);
     full &= full - 1;

@@ -469,9 +469,10 @@ hipError_t launch_combine(const AttnParams& p, int heads, int head_dim, bool f32
 }
 
 hipError_t launch_attention(const AttnParams& p, int heads, int head_dim, bool f32io, hipStream_t stream) {
-  // bf16 softmax attention has its own kernel; fp32 activations and the
-  // logits / top-1 exports use the generic one
-  if (!f32io && !p.logits && !p.top1) return launch_attention_bf16(p, heads, head_dim, stream);
+  // bf16 activations: their own kernel, whose logits / top-1 exports are
+  // compile-time variants of the same tile loop; fp32 activations: the
+  // generic kernel
+  if (!f32io) return launch_attention_bf16(p, heads, head_dim, stream);
   if (head_dim == 128) return f32io ? launch_d<128, true>(p, heads, stream) : launch_d<128, false>(p, heads, stream);
   return f32io ? launch_d<64, true>(p, heads, stream) : launch_d<64, false>(p, heads, stream);
 }

@@ -167,13 +167,19 @@ __device__ __forceinline__ CachePart part_at(const PartTable& t, int e) {
 }
 static_assert(kMaxParts == 16, "part_at covers 16 parts");
 
+// What a launch of the single-cache kernel produces: softmax attention (the
+// product), or, from the same tile rebuild and the same S = Q' K~^T, the
+// scaled logits [H][n_q][n_k] or each query's top-1 token (debug and
+// measurement exports; these run with one workgroup per whole pair).
+enum Export { kAttend = 0, kLogits = 1, kTop1 = 2 };
+
 // One segment: pair (head, query block), key tiles [tb, te).  slot < 0: the
 // segment covers the pair's whole key range (final output), else partial.
 // MULTI: the key axis runs through the parts of the table (compressed caches,
 // then the local chunk).  The segment then runs the pipelined tile loop once
 // per part it touches, with that part's fields fixed (the loop restarts at a
 // part boundary), and forms U^T q again on entering another epoch.
-template <int D, int NPS, int NW, bool MULTI>
+template <int D, int NPS, int NW, bool MULTI, int EX = kAttend>
 __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& gr, const PartTable* tp,
                                                _Float16* lds, int pair, int tb, int te, int slot) {
   // tp: read by the multi-part instantiation only (null in the other)
@@ -319,6 +325,10 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 
   float m_run = -INFINITY;  // running max, log2 units
   float l_run = 0.f;        // this lane's share of the sum of probabilities
+  // top-1 export: this lane's best raw score and its key (its keys arrive in
+  // increasing order, so a strict comparison keeps the lowest key of a tie)
+  float best = -INFINITY;
+  int best_k = 0;
   f32x16 o[NDB];
 #pragma unroll
   for (int b = 0; b < NDB; ++b)
@@ -475,55 +485,72 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
             for (int i = 0; i < 16; ++i)
               if (t0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3) >= tend) s[mb][i] = -INFINITY;
         }
-        // ---- online softmax, base 2 ----
-        float mx = s[0][0];
+        if constexpr (EX != kAttend) {
+          // exports: keys 32 mb + 8 (i / 4) + 4 hf + i % 4 of this tile (the
+          // mapping of the softmax below), masked past the part's end
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-          l_run *= alpha;
+            for (int i = 0; i < 16; ++i) {
+              const int key = t0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
+              if constexpr (EX == kLogits) {
+                if (qvalid && key < tend) p.logits[((int64_t)h * p.n_q + qi) * p.n_k + key] = s[mb][i] * p.scale;
+              } else {
+                if (key < tend && s[mb][i] > best) { best = s[mb][i]; best_k = key; }
+              }
+            }
+          rebuild((j + 1) & 1, ra);
+        } else {
+          // ---- online softmax, base 2 ----
+          float mx = s[0][0];
 #pragma unroll
-          for (int b = 0; b < NDB; ++b)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
-          m_run = m_new;
-        }
-        const float moff = -m_run;
-        h8_t pf[4];
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+          if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+            l_run *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int b = 0; b < NDB; ++b)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            pf[2 * mb + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, moff));
-        // the sum uses the rounded probabilities that enter P V (exact products, fp32 sum)
-        const h2_t one = h2_t{(_Float16)1.f, (_Float16)1.f};
+              for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
+            m_run = m_new;
+          }
+          const float moff = -m_run;
+          h8_t pf[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
-        // rebuild of the next tile into the other buffer: independent VALU work
-        // for the scheduler to place among the P V MFMAs
-        rebuild((j + 1) & 1, ra);
-        // ---- O^T += V~^T P^T, V~ fragments read two MFMAs ahead ----
-        constexpr int NV = 4 * NDB;
-        auto vfrag = [&](int f) {
-          const int c = f / NDB, b = f % NDB;
-          const _Float16* va = vt + (16 * c + trow) * VROW + 32 * b + tcol;
-          const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va));
-          const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va + 8 * VROW));
-          return __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        h8_t vw[2] = {vfrag(0), vfrag(1)};
+            for (int i = 0; i < 16; ++i)
+              pf[2 * mb + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, moff));
+          // the sum uses the rounded probabilities that enter P V (exact products, fp32 sum)
+          const h2_t one = h2_t{(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
-        for (int f = 0; f < NV; ++f) {
-          const int c = f / NDB, b = f % NDB;
-          const h8_t a = vw[f & 1];
-          if (f + 2 < NV) vw[f & 1] = vfrag(f + 2);
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) l_run = __builtin_amdgcn_fdot2(h2_t{pf[c][2 * k], pf[c][2 * k + 1]}, one, l_run, false);
+          // rebuild of the next tile into the other buffer: independent VALU work
+          // for the scheduler to place among the P V MFMAs
+          rebuild((j + 1) & 1, ra);
+          // ---- O^T += V~^T P^T, V~ fragments read two MFMAs ahead ----
+          constexpr int NV = 4 * NDB;
+          auto vfrag = [&](int f) {
+            const int c = f / NDB, b = f % NDB;
+            const _Float16* va = vt + (16 * c + trow) * VROW + 32 * b + tcol;
+            const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va));
+            const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va + 8 * VROW));
+            return __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          h8_t vw[2] = {vfrag(0), vfrag(1)};
+#pragma unroll
+          for (int f = 0; f < NV; ++f) {
+            const int c = f / NDB, b = f % NDB;
+            const h8_t a = vw[f & 1];
+            if (f + 2 < NV) vw[f & 1] = vfrag(f + 2);
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[b], 0, 0, 0);
+          }
         }
       } else {
         rebuild((j + 1) & 1, ra);
@@ -568,6 +595,14 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
   }
 
   if (!wave_active) return;
+  if constexpr (EX == kTop1) {
+    // the two lane halves hold the same query's two key subsets
+    const float ob = __shfl_xor(best, 32);
+    const int ok = __shfl_xor(best_k, 32);
+    if (ob > best || (ob == best && ok < best_k)) best_k = ok;
+    if (qvalid && hf == 0) p.top1[(int64_t)h * p.n_q + qi] = best_k;
+  }
+  if constexpr (EX != kAttend) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
@@ -629,7 +664,7 @@ __device__ __forceinline__ void attend_segment(const AttnParams& p, const Grid& 
 
 // MULTI: the key axis runs through the parts of the table (a separate
 // kernel, so the single-cache one carries none of their code or arguments)
-template <int D, int NPS, int NW, bool MULTI>
+template <int D, int NPS, int NW, bool MULTI, int EX = kAttend>
 __device__ __forceinline__ void attn_bf16_body(const AttnParams& p, const Grid& gr, const PartTable* tbl) {
   constexpr int BUF = BN * kKRow<D, NPS> + BN * (D + 32);
   __shared__ __align__(16) _Float16 lds[2 * BUF];
@@ -637,7 +672,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnParams& p, const Grid& 
   const int w = (bid & 7) * gr.per_xcd + (bid >> 3);
   if (w >= gr.G) return;
   if (gr.ntiles == 0) {  // no keys at all: every pair writes zeros and lse = -inf
-    attend_segment<D, NPS, NW, MULTI>(p, gr, tbl, lds, w, 0, 0, -1);
+    attend_segment<D, NPS, NW, MULTI, EX>(p, gr, tbl, lds, w, 0, 0, -1);
     return;
   }
   const long long u0 = (long long)w * gr.units / gr.G;
@@ -649,7 +684,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnParams& p, const Grid& 
     const int tb = (int)(u % gr.ntiles);
     const int te = (int)min<long long>(gr.ntiles, tb + (u1 - u));
     const int slot = (tb == 0 && te == gr.ntiles) ? -1 : (first ? 2 * w : 2 * w + 1);
-    attend_segment<D, NPS, NW, MULTI>(p, gr, tbl, lds, pair, tb, te, slot);
+    attend_segment<D, NPS, NW, MULTI, EX>(p, gr, tbl, lds, pair, tb, te, slot);
     u += te - tb;
     first = false;
     __syncthreads();  // the next segment's first rebuild reuses buffer 0
@@ -664,6 +699,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnParams p
 template <int D, int NPS, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_multi_kernel(AttnParams p, Grid gr, PartTable tbl) {
   attn_bf16_body<D, NPS, NW, true>(p, gr, &tbl);
+}
+
+// The logits / top-1 exports of the single-cache kernel (EX: kLogits, kTop1)
+template <int D, int NPS, int NW, int EX>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_export_kernel(AttnParams p, Grid gr) {
+  attn_bf16_body<D, NPS, NW, false, EX>(p, gr, nullptr);
 }
 
 // Workgroup w whose units [w U / G, (w + 1) U / G) hold unit x (U >= G).
@@ -730,7 +771,11 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(AttnParams p, Grid gr) 
 }
 
 template <int D, int NPS>
-hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream, const PartTable* parts) {
+hipError_t launch_t(const AttnParams& p_in, int heads, hipStream_t stream, const PartTable* parts) {
+  // the exports take whole pairs (no partial results, no combine pass)
+  const int ex = p_in.logits ? kLogits : (p_in.top1 ? kTop1 : kAttend);
+  AttnParams p = p_in;
+  if (ex != kAttend) p.part_o = nullptr;
   constexpr int BM = 32 * kWaves;               // queries per workgroup
   const int max_wg = kAttnBf16MaxWorkgroups * 8 / kWaves;  // one CU's worth per 8 waves
   Grid g;
@@ -769,14 +814,20 @@ hipError_t launch_t(const AttnParams& p, int heads, hipStream_t stream, const Pa
     const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(p.ev_begin), stream);
     if (er != hipSuccess) return er;
   }
-  if (parts)
+  if (ex == kLogits)
+    hipLaunchKernelGGL((attn_bf16_export_kernel<D, NPS, kWaves, kLogits>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0,
+                       stream, p, g);
+  else if (ex == kTop1)
+    hipLaunchKernelGGL((attn_bf16_export_kernel<D, NPS, kWaves, kTop1>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0,
+                       stream, p, g);
+  else if (parts)
     hipLaunchKernelGGL((attn_bf16_multi_kernel<D, NPS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g,
                        tbl);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, NPS, kWaves>), dim3(g.per_xcd * 8), dim3(64 * kWaves), 0, stream, p, g);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.ev_end) e = hipEventRecord(static_cast<hipEvent_t>(p.ev_end), stream);
-  if (e != hipSuccess || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
+  if (e != hipSuccess || ex != kAttend || g.G <= 1 || !p.part_o || g.ntiles == 0) return e;
   hipLaunchKernelGGL((combine_sk_kernel<D>), dim3((unsigned)pairs, (g.qpb + kCombineRows<D> - 1) / kCombineRows<D>),
                      dim3(256), 0, stream, p, g);
   return hipGetLastError();

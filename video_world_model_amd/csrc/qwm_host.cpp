@@ -21,6 +21,8 @@ namespace {
 
 thread_local hipError_t g_last_hip = hipSuccess;
 thread_local std::string g_msg;
+// device uint32[4] that appends add their path counts to (null: none)
+uint32_t* g_path_counters = nullptr;
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -539,6 +541,12 @@ QWM_API int qwm_calibrate(const qwm_config* cfg, void* calib, const void* q_hist
   return qwm_calib_import_moment(cfg, calib, m.data(), stream);
 }
 
+QWM_API int qwm_append_path_counters(void* counters) {
+  if (counters && ((uintptr_t)counters & 3u)) return QWM_ERR_INVALID_ARG;
+  g_path_counters = static_cast<uint32_t*>(counters);
+  return QWM_OK;
+}
+
 QWM_API int qwm_cache_init(const qwm_config* cfg, const void* calib, void* base, qwm_cache* cache) {
   const int st = check_config(cfg);
   if (st) return st;
@@ -628,6 +636,7 @@ int fill_append(const qwm_config* cfg, const qwm_cache* cache, const void* x, in
   p.rp = rpitch(cfg->rank);
   p.sgroup = reinterpret_cast<const double*>(kb + L.sgroup);
   p.head_max = reinterpret_cast<const float*>(kb + L.head_max);
+  p.counters = g_path_counters;
   return QWM_OK;
 }
 
@@ -908,8 +917,9 @@ QWM_API int qwm_attention_logits(const qwm_config* cfg, const qwm_cache* cache, 
   if (s) return s;
   if (!logits && n_q > 0 && cache->n_k > 0) return QWM_ERR_INVALID_ARG;
   if (n_q == 0 || cache->n_k == 0) return QWM_OK;
-  // the debug variant runs the same tile rebuild and S = Q'K~^T, exports the
-  // scaled logits and stores no attention output
+  // the debug variant of the attention kernel that the activations' dtype
+  // selects (the bf16 kernel, or the fp32 one): the same tile rebuild and
+  // S = Q' K~^T, exporting the scaled logits instead of the attention output
   p.logits = logits;
   p.out = nullptr;
   hipError_t e = qwm::launch_attention(p, cfg->num_heads, cfg->head_dim, cfg->io_dtype == QWM_F32,

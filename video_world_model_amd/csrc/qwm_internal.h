@@ -51,6 +51,11 @@ struct AppendParams {
   int8_t* coef;      // [H][Ncap][r]
   uint16_t* coef_scale;  // [H][Ncap] fp16 bits
   int64_t tok0;      // first cache token index of this append
+  // optional path counters (device, uint32[4], nullable): tokens whose
+  // candidate set was settled by exact rescoring of the screen's uncertain
+  // band, and tokens that searched all centres; [0], [1] for Keys, [2], [3]
+  // for Values
+  uint32_t* counters;
 };
 
 // Attention over the compressed cache.
@@ -135,9 +140,10 @@ QWM_HIDDEN hipError_t launch_append_kv(const AppendParams& pk, const AppendParam
                                        bool f32io, hipStream_t stream);
 QWM_HIDDEN hipError_t launch_attention(const AttnParams& p, int heads, int head_dim, bool f32io,
                                        hipStream_t stream);
-// bf16 activations, softmax attention only (no logits / top-1 export); with a
-// part table (several compressed caches and / or the local chunk: p.n_loc),
-// the key axis runs through the parts in order
+// bf16 activations: softmax attention, or (p.logits / p.top1 set) the logits
+// or top-1 export of the same kernel; with a part table (several compressed
+// caches and / or the local chunk: p.n_loc), the key axis runs through the
+// parts in order
 QWM_HIDDEN hipError_t launch_attention_bf16(const AttnParams& p, int heads, int head_dim, hipStream_t stream,
                                             const PartTable* parts = nullptr);
 QWM_HIDDEN hipError_t launch_combine(const AttnParams& p, int heads, int head_dim, bool f32io, hipStream_t stream);

@@ -177,3 +177,13 @@ def generate(w: Workload, heads=None, frames=None, threads: int = 8) -> dict:
     qh = _stack_heads(lambda h: queries(w, h, w.n_q_hist, True), heads, threads)
     nh = min(w.n_kv_hist, k.shape[1])
     return dict(k=k, v=v, q=q, q_hist=qh, k_hist=k[:, :nh], v_hist=v[:, :nh])
+
+
+def frame_bits(job) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) [heads, F, d] of one frame of K or V for
+    every head of a bf16 workload: job = (workload, "k" or "v", frame).  The
+    same values as kv_frames, in a form that is cheap to pass between worker
+    processes and to copy to a bfloat16 device tensor."""
+    w, which, f = job
+    x = np.stack([kv_frames(w, h, which, f, f + 1) for h in range(w.heads)])
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
