@@ -321,6 +321,24 @@ int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, 
                   const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
                   float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * qwm_attention for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (minus the workspace), results and
+ * errors as qwm_attention with a workspace of QWM_NOALLOC_SCRATCH_BYTES; the
+ * partial results go to a device array inside the library instead (32.5 MiB,
+ * held on every GPU the library runs on until the process ends; enough for
+ * the stream-K partials of bf16 activations at head_dim 128, else
+ * QWM_ERR_CAPACITY).  No allocation happens in the call.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and give wrong results.  Nothing in the array needs
+ * clearing: each partial result is written before it is read in the same call.
+ */
+#define QWM_NOALLOC_SCRATCH_BYTES 34078720u
+int qwm_attention_noalloc(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                          const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
+                          float* lse, void* stream);
+
 /* qwm_attention with two optional HIP events (hipEvent_t, NULL to skip)
  * recorded on stream immediately before and after the main attention kernel,
  * so that its duration can be measured apart from the pass that merges

@@ -25,7 +25,8 @@ EXPORTS = ["qwm_abi_version", "qwm_status_string", "qwm_layout", "qwm_footprint"
            "qwm_calib_import", "qwm_calib_import_moment", "qwm_calibrate", "qwm_cache_init", "qwm_quantize_append_k",
            "qwm_quantize_append_v", "qwm_quantize_append_kv", "qwm_attention_workspace_size", "qwm_attention",
            "qwm_attention_timed", "qwm_attention_local", "qwm_attention_epochs", "qwm_attention_logits", "qwm_top1", "qwm_dense_top1",
-           "qwm_append_path_counters"]
+           "qwm_append_path_counters", "qwm_attention_noalloc"]
+NOALLOC_SCRATCH_BYTES = 34078720
 
 
 class QwmConfig(ctypes.Structure):
@@ -98,6 +99,7 @@ def lib():
             "qwm_top1": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, P, P]),
             "qwm_dense_top1": (ctypes.c_int, [CFG, P, I64, ST, P, I64, ST, P, P]),
             "qwm_append_path_counters": (ctypes.c_int, [P]),
+            "qwm_attention_noalloc": (ctypes.c_int, [CFG, ctypes.POINTER(QwmCache), P, I64, ST, F, P, ST, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -426,6 +428,21 @@ def attention(cache: Cache, q, out=None, lse=None, workspace=None, scale: float 
                                         ctypes.byref(sq), scale, _ptr(out), ctypes.byref(so), _ptr(lse),
                                         _ptr(workspace), nb, _stream(), ctypes.c_void_p(e0.cuda_event),
                                         ctypes.c_void_p(e1.cuda_event)))
+    return out, lse
+
+
+def attention_noalloc(cache: Cache, q, out, lse, scale: float = 0.0):
+    """qwm_attention_noalloc: attention of q over the cache with the partial
+    results in the library's own device array (no workspace, no allocation;
+    out and lse are the caller's).  Calls that overlap on one GPU race."""
+    cfg = cache.cfg
+    check_activation(cfg, q, "q")
+    import torch
+    _check_outputs(cfg, q, out, lse, None)
+    c = cfg.c()
+    sq, so = strides(q), strides(out)
+    check(lib().qwm_attention_noalloc(ctypes.byref(c), ctypes.byref(cache.handle), _ptr(q), q.shape[1],
+                                      ctypes.byref(sq), scale, _ptr(out), ctypes.byref(so), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -901,6 +902,54 @@ QWM_API int qwm_attention_epochs(const qwm_config* cfg, const qwm_cache* caches,
                                  void* stream) {
   return attention_parts(cfg, caches, n_caches, q, n_q, st_q, k_loc, v_loc, n_loc, st_k, st_v, scale, out, st_out,
                          lse, workspace, ws_bytes, stream);
+}
+
+// ------------------------------------------------- allocation-free attention
+// The partial results of qwm_attention_noalloc live in this file-scope device
+// array (each GPU the library runs on holds its own copy until the process
+// ends).  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[QWM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device, with that device current).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return QWM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr) return QWM_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return QWM_OK;
+}
+}  // namespace
+
+QWM_API int qwm_attention_noalloc(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
+                                  const qwm_strides* st_q, float scale, void* out, const qwm_strides* st_out,
+                                  float* lse, void* stream) {
+  int s = check_config(cfg);
+  if (s) return s;
+  // the stream-K partial results of bf16 activations must fit in the array
+  // (fp32 activations split their key range only as far as it holds them)
+  if (cfg->io_dtype == QWM_BF16 && bf16_partial_bytes(cfg) > (size_t)QWM_NOALLOC_SCRATCH_BYTES)
+    return QWM_ERR_CAPACITY;
+  void* ptr = nullptr;
+  if ((s = scratch_address(&ptr))) return s;
+  return qwm_attention_timed(cfg, cache, q, n_q, st_q, scale, out, st_out, lse, ptr,
+                             (size_t)QWM_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
 }
 
 QWM_API int qwm_attention(const qwm_config* cfg, const qwm_cache* cache, const void* q, int64_t n_q,
