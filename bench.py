@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling for profiles)")
     ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--no-rollout", action="store_true",
+                    help="1-minute rollout: append the frames before the timed step without the per-step "
+                         "attention (for profiler runs whose per-kernel averages should cover the timed "
+                         "full-cache launches only)")
     ap.add_argument("--measure-frames", type=int, default=24,
                     help="1-minute rollout: frames of the prefix the quality measures run on")
     ap.add_argument("--epoch-frames", type=int, default=24,
@@ -555,25 +559,38 @@ def generation_step(args, w, qwm, torch, np, workloads, pool):
     lse = torch.empty(H, w.n_q, dtype=torch.float32, device="cuda")
 
     # ---- rollout leg: append frame f, attend over frames 0..f (eager) ----
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nf)]
-    for e in ev:
-        for x in e:
-            x.record()
+    rollout = None
+    if args.no_rollout:
+        for f in range(nf):
+            qwm.append_kv(cache, kd[:, f * F:(f + 1) * F], vd[:, f * F:(f + 1) * F])
+    else:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nf)]
+        for e in ev:
+            for x in e:
+                x.record()
+        torch.cuda.synchronize()
+        for f in range(nf):
+            e = ev[f]
+            e[0].record()
+            qwm.append_kv(cache, kd[:, f * F:(f + 1) * F], vd[:, f * F:(f + 1) * F])
+            e[1].record()
+            qwm.attention(cache, q, out=out, lse=lse, workspace=ws, kernel_events=(e[3], e[4]))
+            e[2].record()
+            if f % 40 == 0:
+                print("[bench] rollout frame %d" % f, file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        r_app = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        r_att = np.array([e[1].elapsed_time(e[2]) for e in ev])
+        r_attk = np.array([e[3].elapsed_time(e[4]) for e in ev])
+        r_tf = np.array([attn_flops(w, w.n_q, (f + 1) * F) for f in range(nf)]) / (r_attk * 1e-3) / 1e12
+        rollout = {"steps": nf, "append_ms_median": round(float(np.median(r_app)), 4),
+                   "attention_ms_median": round(float(np.median(r_att)), 4),
+                   "attention_ms_final": round(float(r_att[-1]), 4),
+                   "attention_tflops_final": round(float(r_tf[-1]), 2),
+                   "attention_tflops_steady_median": round(float(np.median(r_tf[len(r_tf) // 2:])), 2),
+                   "total_ms": round(float(r_app.sum() + r_att.sum()), 2),
+                   "launch": "eager, one append and one attention call per generated frame"}
     torch.cuda.synchronize()
-    for f in range(nf):
-        e = ev[f]
-        e[0].record()
-        qwm.append_kv(cache, kd[:, f * F:(f + 1) * F], vd[:, f * F:(f + 1) * F])
-        e[1].record()
-        qwm.attention(cache, q, out=out, lse=lse, workspace=ws, kernel_events=(e[3], e[4]))
-        e[2].record()
-        if f % 40 == 0:
-            print("[bench] rollout frame %d" % f, file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    r_app = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    r_att = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    r_attk = np.array([e[3].elapsed_time(e[4]) for e in ev])
-    r_tf = np.array([attn_flops(w, w.n_q, (f + 1) * F) for f in range(nf)]) / (r_attk * 1e-3) / 1e12
 
     # ---- the timed generation step at the full cache ----
     n_prev = (nf - 1) * F
@@ -680,13 +697,7 @@ def generation_step(args, w, qwm, torch, np, workloads, pool):
                      "frac": round(tf / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic_from_profiles("attention", w.name, src_hash),
                      "algorithmic_flops_per_launch": flops, "ms_per_launch": round(attk_ms, 4)},
-        "rollout": {"steps": nf, "append_ms_median": round(float(np.median(r_app)), 4),
-                    "attention_ms_median": round(float(np.median(r_att)), 4),
-                    "attention_ms_final": round(float(r_att[-1]), 4),
-                    "attention_tflops_final": round(float(r_tf[-1]), 2),
-                    "attention_tflops_steady_median": round(float(np.median(r_tf[len(r_tf) // 2:])), 2),
-                    "total_ms": round(float(r_app.sum() + r_att.sum()), 2),
-                    "launch": "eager, one append and one attention call per generated frame"},
+        "rollout": rollout,
         "compression": {"ratio": round(original / stored, 4), "ratio_resident": round(original / resident, 4),
                         "stored_bytes": stored, "resident_bytes": resident, "original_bytes": original},
         "top8_energy_mean": round(float(energy.mean()), 4),
