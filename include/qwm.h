@@ -381,14 +381,14 @@ int qwm_attention_local(const qwm_config* cfg, const qwm_cache* cache, const voi
  * may calibrate again from recent frames and start a new cache block with the
  * new calibration for the frames that follow, so every stored frame keeps
  * the centres and U it was encoded with.  caches (host array, oldest first)
- * holds n_caches in [1, 16] such handles of the same cfg, each bound to its
+ * holds n_caches in [1, 64] such handles of the same cfg, each bound to its
  * own calibration block; their tokens, then the optional local chunk k_loc,
  * v_loc as in qwm_attention_local, form the key axis of one softmax:
  *   k~_t = mu_K^e[idx_t] + rho_hat_t + u^e (coef_t coef_scale_t) for a token
  *   t of epoch e (v~_t likewise with mu_V^e), out and lse as for
  *   qwm_attention_local.
  * One launch; U^T q is formed per epoch.  Every handle needs n_k == n_v (else
- * QWM_ERR_STATE); empty epochs are allowed.  n_caches > 16:
+ * QWM_ERR_STATE); empty epochs are allowed.  n_caches > 64:
  * QWM_ERR_UNSUPPORTED; n_caches < 1 or caches NULL: QWM_ERR_INVALID_ARG.
  * bf16 activations only.  Workspace: qwm_attention_workspace_size(cfg,
  * total tokens, n_q).  With n_caches = 1 this is qwm_attention_local.

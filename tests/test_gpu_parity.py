@@ -622,6 +622,40 @@ def test_epochs_edge_cases():
     assert wo <= 1.0 and wl <= 1.0
 
 
+
+def test_epochs_most_parts():
+    """Sixty-four epochs, the most one call takes (one frame in four of them,
+    the others empty), against the oracle."""
+    import video_world_model_amd as qwm
+    w = workloads.scaled(W["matrix_game"], heads=1, frames=4)
+    cfg = P.cfg_of(w, max_frames=1)
+    F = w.frame_tokens
+    say("case epochs_64")
+    data = case_data(w)
+    cal = P.oracle_calibration(w, data, cfg, iters=2)
+    where = {0: 0, 17: 1, 40: 2, 63: 3}
+    caches, rebuilt = [], []
+    for e in range(64):
+        f = where.get(e)
+        if f is None:
+            caches.append(_epoch_cache(cfg, cal, data["k"][:, :0], data["v"][:, :0]))
+            continue
+        k_e, v_e = data["k"][:, f * F:(f + 1) * F], data["v"][:, f * F:(f + 1) * F]
+        cache = _epoch_cache(cfg, cal, k_e, v_e)
+        caches.append(cache)
+        gpu = P.gpu_fields(cache, F)
+        stats = P.Stats()
+        ko = P.check_keys_head(cfg, k_e[0], cal, 0, gpu, stats)
+        vo = P.check_values_head(cfg, v_e[0], cal, 0, gpu, stats)
+        _, _, kr, vr = P.oracle_attention(cfg, cal, 0, ko, vo, data["q"][0][:1])
+        rebuilt.append((kr, vr, P.logit_error_bound(cfg, cal, 0, ko, data["q"][0][:200].astype(np.float64))))
+    q = P.to_dev(data["q"][:, :200], cfg)
+    o, lse = qwm.attention_epochs(caches, q)
+    wo, wl = P.check_parts(data["q"][0][:200].astype(np.float64), rebuilt, o[0].float().cpu().numpy(),
+                           lse[0].cpu().numpy())
+    say("  64 epochs: %.3g %.3g" % (wo, wl))
+    assert wo <= 1.0 and wl <= 1.0
+
 def test_degenerate_inputs_zero_residual_and_tied_centres():
     """Keys and Values that sit exactly on their centres (zero residual: every
     tile scale 0, every code 0, every PSAC scale 0) mixed with ordinary tokens,

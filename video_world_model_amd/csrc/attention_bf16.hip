@@ -159,13 +159,25 @@ __device__ __forceinline__ CachePart part_at(const PartTable& t, int e) {
     QWM_PART_CASE(0) QWM_PART_CASE(1) QWM_PART_CASE(2) QWM_PART_CASE(3)
     QWM_PART_CASE(4) QWM_PART_CASE(5) QWM_PART_CASE(6) QWM_PART_CASE(7)
     QWM_PART_CASE(8) QWM_PART_CASE(9) QWM_PART_CASE(10) QWM_PART_CASE(11)
-    QWM_PART_CASE(12) QWM_PART_CASE(13) QWM_PART_CASE(14)
+    QWM_PART_CASE(12) QWM_PART_CASE(13) QWM_PART_CASE(14) QWM_PART_CASE(15)
+    QWM_PART_CASE(16) QWM_PART_CASE(17) QWM_PART_CASE(18) QWM_PART_CASE(19)
+    QWM_PART_CASE(20) QWM_PART_CASE(21) QWM_PART_CASE(22) QWM_PART_CASE(23)
+    QWM_PART_CASE(24) QWM_PART_CASE(25) QWM_PART_CASE(26) QWM_PART_CASE(27)
+    QWM_PART_CASE(28) QWM_PART_CASE(29) QWM_PART_CASE(30) QWM_PART_CASE(31)
+    QWM_PART_CASE(32) QWM_PART_CASE(33) QWM_PART_CASE(34) QWM_PART_CASE(35)
+    QWM_PART_CASE(36) QWM_PART_CASE(37) QWM_PART_CASE(38) QWM_PART_CASE(39)
+    QWM_PART_CASE(40) QWM_PART_CASE(41) QWM_PART_CASE(42) QWM_PART_CASE(43)
+    QWM_PART_CASE(44) QWM_PART_CASE(45) QWM_PART_CASE(46) QWM_PART_CASE(47)
+    QWM_PART_CASE(48) QWM_PART_CASE(49) QWM_PART_CASE(50) QWM_PART_CASE(51)
+    QWM_PART_CASE(52) QWM_PART_CASE(53) QWM_PART_CASE(54) QWM_PART_CASE(55)
+    QWM_PART_CASE(56) QWM_PART_CASE(57) QWM_PART_CASE(58) QWM_PART_CASE(59)
+    QWM_PART_CASE(60) QWM_PART_CASE(61) QWM_PART_CASE(62) QWM_PART_CASE(63)
 #undef QWM_PART_CASE
     default:
       return t.part[kMaxParts - 1];
   }
 }
-static_assert(kMaxParts == 16, "part_at covers 16 parts");
+static_assert(kMaxParts == 64, "part_at covers 64 parts");
 
 // What a launch of the single-cache kernel produces: softmax attention (the
 // product), or, from the same tile rebuild and the same S = Q' K~^T, the

@@ -117,7 +117,7 @@ struct AttnParams {
 // starts at a tile boundary; a part's keys run from 0 to n_k in its own cache.
 // Every part has the same configuration, so the fields sit at the same byte
 // offsets inside each cache block and each calibration block.
-constexpr int kMaxParts = 16;
+constexpr int kMaxParts = 64;
 struct CachePart {
   const unsigned char* cache;  // cache block
   const unsigned char* calib;  // its calibration block
