@@ -163,6 +163,20 @@ def traffic_from_profiles(kernel, config, src_hash):
     return d.get("hbm_bytes_per_launch")
 
 
+def query_blocks(w):
+    """Query blocks per head of the attention launch: each reads the whole
+    compressed cache of its head once (blocks of at most 256 queries, balanced
+    and rounded up to whole 32-query waves)."""
+    return -(-w.n_q // 256)
+
+
+def counter_gbs(kernel, config, src_hash, ms):
+    """HBM GB/s of the kernel from the committed counter traffic (None when
+    the counters were taken on other sources)."""
+    t = traffic_from_profiles(kernel, config, src_hash)
+    return None if t is None else round(t / (ms * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(w, data, cfg_host, heads, seed):
     """The oracle (untuned) on a bounded sample: append + attention of
     `heads` heads of the same workload, scaled to Ktokens/s of the full step."""
@@ -382,7 +396,9 @@ def main():
                       "combine_ms": round(max(att_avg - attk_avg, 0.0), 4), "tflops": round(achieved_tf, 2),
                       "frac_mfma": round(achieved_tf / PEAK_FP16_TFLOPS, 4),
                       "flops_per_launch": flops,
-                      "compressed_cache_gbs": round(stored / (attk_avg * 1e-3) / 1e9, 2)},
+                      "compressed_cache_gbs": round(stored / (attk_avg * 1e-3) / 1e9, 2),
+                      "compressed_cache_streamed_gbs": round(stored * query_blocks(w) / (attk_avg * 1e-3) / 1e9, 2),
+                      "counter_hbm_gbs": counter_gbs("attention", w.name, src_hash, attk_avg)},
         "attention_local": {"ms": round(loc_ms, 4), "local_tokens": F, "tflops": round(loc_tf, 2),
                             "frac_mfma": round(loc_tf / PEAK_FP16_TFLOPS, 4),
                             "flops_per_call": attn_flops(w, w.n_q, w.n_tokens + F)},
@@ -689,7 +705,9 @@ def generation_step(args, w, qwm, torch, np, workloads, pool):
         "attention": {"kernel_ms": round(attk_ms, 4), "call_ms": round(att_call_ms, 4),
                       "tflops": round(tf, 2), "frac_mfma": round(tf / PEAK_FP16_TFLOPS, 4),
                       "flops_per_launch": flops,
-                      "compressed_cache_gbs": round(stored / (attk_ms * 1e-3) / 1e9, 2)},
+                      "compressed_cache_gbs": round(stored / (attk_ms * 1e-3) / 1e9, 2),
+                      "compressed_cache_streamed_gbs": round(stored * query_blocks(w) / (attk_ms * 1e-3) / 1e9, 2),
+                      "counter_hbm_gbs": counter_gbs("attention", w.name, src_hash, attk_ms)},
         "attention_local": {"ms": round(loc_ms, 4), "local_tokens": F, "tflops": round(loc_tf, 2),
                             "frac_mfma": round(loc_tf / PEAK_FP16_TFLOPS, 4)},
         "roofline": {"kernel": "attn_bf16_kernel (dequant-attention, full cache)", "bound": "mfma",
