@@ -480,14 +480,14 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline_generation_step(w, seed, prefix):
+def cpu_baseline_generation_step(w, seed, heads=2, prefix=60):
     """The oracle (untuned) on a bounded sample of the generation step: for
-    head 0, the quantize-append of the newest frame (Keys and Values) and the
-    attention of the query chunk over the rebuilt first `prefix` frames (the
-    rebuild from the stored fields plus the softmax).  The attention part is
-    scaled to all cached frames (its cost is linear in the cached tokens) and
-    the whole to all heads.  The oracle's append of the prefix frames is
-    untimed setup."""
+    the first `heads` heads, the quantize-append of the newest frame (Keys and
+    Values) and the attention of the query chunk over the rebuilt first
+    `prefix` cached frames (the rebuild from the stored fields plus the
+    softmax).  The attention part is scaled to all cached frames (its cost is
+    linear in the cached tokens) and the whole to all heads.  The oracle's
+    append of the prefix frames is untimed setup."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
 
@@ -496,40 +496,46 @@ def cpu_baseline_generation_step(w, seed, prefix):
     from oracle import calibrate as oc
     from oracle import codec
     F, T, nf = w.frame_tokens, w.group_tokens, w.frames
-    k0 = workloads.kv_frames(w, 0, "k", 0, prefix)
-    v0 = workloads.kv_frames(w, 0, "v", 0, prefix)
-    k_last = workloads.kv_frames(w, 0, "k", nf - 1, nf)
-    v_last = workloads.kv_frames(w, 0, "v", nf - 1, nf)
-    q0 = workloads.queries(w, 0, w.n_q, historical=False)
-    qh0 = workloads.queries(w, 0, w.n_q_hist, historical=True)
-    cal = oc.calibrate(qh0[None], k0[None, :F], v0[None, :F], w.c_k, w.c_v, w.rank, w.io, seed=seed, iters=2)
-    mk, mv, sk, uk = cal["mu_k"][0], cal["mu_v"][0], cal["sens"][0], cal["u"][0]
+    prefix = min(prefix, nf - 1)
+    t_app = t_att = 0.0
+    for h in range(heads):
+        k0 = workloads.kv_frames(w, h, "k", 0, prefix)
+        v0 = workloads.kv_frames(w, h, "v", 0, prefix)
+        k_last = workloads.kv_frames(w, h, "k", nf - 1, nf)
+        v_last = workloads.kv_frames(w, h, "v", nf - 1, nf)
+        q0 = workloads.queries(w, h, w.n_q, historical=False)
+        qh0 = workloads.queries(w, h, w.n_q_hist, historical=True)
+        cal = oc.calibrate(qh0[None], k0[None, :F], v0[None, :F], w.c_k, w.c_v, w.rank, w.io, seed=seed + 2 * h, iters=2)
+        mk, mv, sk, uk = cal["mu_k"][0], cal["mu_v"][0], cal["sens"][0], cal["u"][0]
 
-    def append(f, k, v):
-        return f, codec.append_keys(k, mk, sk, uk, F, T, w.top_k, 0), codec.append_values(v, mv, F, T)
-    with ThreadPoolExecutor(8) as ex:
-        parts = sorted(ex.map(lambda f: append(f, k0[f * F:(f + 1) * F], v0[f * F:(f + 1) * F]), range(prefix)),
-                       key=lambda x: x[0])
-    ko = {key: np.concatenate([p[1][key] for p in parts]) for key in ("idx", "codes", "z", "s", "coef", "coef_scale")}
-    vo = {key: np.concatenate([p[2][key] for p in parts]) for key in ("idx", "codes", "z", "s")}
-    t0 = time.perf_counter()
-    append(nf - 1, k_last, v_last)
-    t_app = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    kr = oa.reconstruct_keys(ko["idx"], ko["codes"], ko["z"], ko["s"], ko["coef"], ko["coef_scale"], mk, uk, F, T)
-    vr = oa.reconstruct_values(vo["idx"], vo["codes"], vo["z"], vo["s"], mv, F, T)
-    oa.softmax_attention(q0, kr, vr)
-    t_att = time.perf_counter() - t0
-    step_s = w.heads * (t_app + t_att * nf / prefix)
+        def append(f, k, v):
+            return f, codec.append_keys(k, mk, sk, uk, F, T, w.top_k, 0), codec.append_values(v, mv, F, T)
+        with ThreadPoolExecutor(8) as ex:
+            parts = sorted(ex.map(lambda f: append(f, k0[f * F:(f + 1) * F], v0[f * F:(f + 1) * F]), range(prefix)),
+                           key=lambda x: x[0])
+        ko = {key: np.concatenate([p[1][key] for p in parts]) for key in ("idx", "codes", "z", "s", "coef", "coef_scale")}
+        vo = {key: np.concatenate([p[2][key] for p in parts]) for key in ("idx", "codes", "z", "s")}
+        del parts
+        t0 = time.perf_counter()
+        append(nf - 1, k_last, v_last)
+        t_app += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        kr = oa.reconstruct_keys(ko["idx"], ko["codes"], ko["z"], ko["s"], ko["coef"], ko["coef_scale"], mk, uk, F, T)
+        vr = oa.reconstruct_values(vo["idx"], vo["codes"], vo["z"], vo["s"], mv, F, T)
+        oa.softmax_attention(q0, kr, vr)
+        t_att += time.perf_counter() - t0
+        del kr, vr
+        print("[bench] oracle baseline head %d done" % h, file=sys.stderr, flush=True)
+    step_s = (t_app + t_att * nf / prefix) * w.heads / heads
     blas = blas_threads()
     cores = len(os.sched_getaffinity(0))
     return {"value": round(w.n_tokens / step_s / 1e3, 4), "unit": "Ktokens/s", "cores": int(min(cores, max(blas, 1))),
             "kind": "oracle", "step_s": round(step_s, 2),
-            "sample": "head 0 of %d at the final generation step: the oracle's quantize-append of the newest frame "
-                      "(%.2f s) and its attention of %d queries over the rebuilt first %d of %d cached frames "
-                      "(%.2f s, scaled x%g to all frames: the cost is linear in the cached tokens); the step "
-                      "scaled x%d to all heads; BLAS threads %d, affinity cores %d"
-                      % (w.heads, t_app, w.n_q, prefix, nf, t_att, nf / prefix, w.heads, blas, cores)}
+            "sample": "heads 0..%d of %d at the final generation step: the oracle's quantize-append of the newest "
+                      "frame (%.2f s in all) and its attention of %d queries over the rebuilt first %d of %d cached "
+                      "frames (%.2f s in all, scaled x%g to all frames: the cost is linear in the cached tokens), "
+                      "timed; the step scaled x%g to all heads; BLAS threads %d, affinity cores %d"
+                      % (heads - 1, w.heads, t_app, w.n_q, prefix, nf, t_att, nf / prefix, w.heads / heads, blas, cores)}
 
 
 def generation_step(args, w, qwm, torch, np, workloads, pool):
@@ -743,7 +749,7 @@ def generation_step(args, w, qwm, torch, np, workloads, pool):
         res["copy_probe_bytes"] = n * 4
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline of the generation step (one head)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline_generation_step(w, args.seed, prefix=args.measure_frames)
+        res["cpu_baseline"] = cpu_baseline_generation_step(w, args.seed)
     print(json.dumps(res), flush=True)
 
 
