@@ -70,3 +70,22 @@ def test_host_calibration_shape_checks():
         qwm.calibrate_host(CFG, q[:1], q, q, seed=1)
     with pytest.raises(ValueError, match="k_hist"):
         qwm.calibrate_host(CFG, q, q, q[:, :10], seed=1)
+
+
+def test_cache_truncate_host_side():
+    """Truncation to whole frames only, never beyond what is cached (host
+    handle only)."""
+    cache = _cache_stub(CFG)
+    cache.handle.n_k = cache.handle.n_v = 32  # two frames of 16 tokens
+    with pytest.raises(ValueError, match="whole number of frames"):
+        cache.truncate(8)
+    with pytest.raises(ValueError, match="whole number of frames"):
+        cache.truncate(48)
+    with pytest.raises(ValueError, match="whole number of frames"):
+        cache.truncate(-16)
+    cache.truncate(16)
+    assert (cache.handle.n_k, cache.handle.n_v) == (16, 16)
+    cache.truncate(16)
+    assert cache.n_k == cache.n_v == 16
+    cache.truncate(0)
+    assert (cache.handle.n_k, cache.handle.n_v) == (0, 0)
